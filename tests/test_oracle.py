@@ -1,0 +1,537 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: each check uses a value the pages
+print, a closed form, a library routine, or brute force written separately in
+pure Python.  The mutation tests at the end plant plausible mistakes in copies of
+the oracle's arithmetic and confirm that at least one pin catches each.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import softmax as scipy_softmax
+
+import oracle
+from oracle import ring_oracle as ro
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand_qkv(rng, N, Hq, Hkv, d, scale=1.0):
+    q = rng.standard_normal((N, Hq, d))
+    k = rng.standard_normal((N, Hkv, d)) * scale
+    v = rng.standard_normal((N, Hkv, d))
+    return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# Worked example with printed values.
+# ---------------------------------------------------------------------------
+
+def _worked_example_errors():
+    g = _load("worked_example.json")
+    Q = np.array(g["Q"], float).reshape(4, 1, 1)
+    K = np.array(g["K"], float).reshape(4, 1, 1)
+    V = np.array(g["V"], float).reshape(4, 1, 1)
+    want = np.array(g["outputs"])
+    P, b = 2, 2
+    ring_out = np.zeros(4)
+    for u in range(P):
+        o, _ = ro.ring_forward(Q[u * b:(u + 1) * b], u, K, V, P, "contiguous", False)
+        ring_out[u * b:(u + 1) * b] = o[:, 0, 0]
+    dense_out, _ = ro.dense_attention(Q, np.arange(4), K, V, False)
+    _, _, states = ro.ring_forward(Q[0:2], 0, K, V, P, "contiguous", False, trace=True)
+    trace_err = 0.0
+    for (r, m, z, y), key in zip(states, ["after_step0", "after_step1"]):
+        st = g["q1_on_device0"][key]
+        trace_err = max(trace_err, abs(m[0, 0] - st["m"]), abs(z[0, 0] - st["l"]),
+                        abs(y[0, 0, 0] - st["acc"]))
+    visited = [r for (r, *_rest) in states]
+    return (np.abs(ring_out - want).max(), np.abs(dense_out[:, 0, 0] - want).max(),
+            trace_err, visited)
+
+
+def test_worked_example_outputs_and_trace():
+    ring_err, dense_err, trace_err, visited = _worked_example_errors()
+    # outputs printed to 5 decimals, the running state to 6
+    assert ring_err <= 5e-6 + 1e-12
+    assert dense_err <= 5e-6 + 1e-12
+    assert trace_err <= 5e-7 + 1e-12
+    assert visited == [0, 1]   # device 0: own block, then the neighbour's
+
+
+def test_worked_example_final_value_and_weights():
+    g = _load("worked_example.json")
+    q1 = np.array([[[1.0]]])
+    K = np.array(g["K"], float).reshape(4, 1, 1)
+    V = np.array(g["V"], float).reshape(4, 1, 1)
+    o, lse = ro.dense_attention(q1, np.array([0]), K, V, False)
+    assert abs(o[0, 0, 0] - g["q1_on_device0"]["final"]) <= 5e-7
+    # LSE = max + ln Z, with the page's max 2 and Z = 1.55300
+    assert abs(lse[0, 0] - (2.0 + math.log(g["q1_Z"]))) <= 5e-5
+
+
+# ---------------------------------------------------------------------------
+# Ring recurrence equals the dense definition.
+# ---------------------------------------------------------------------------
+
+RING_CASES = [
+    # layout, causal, P, b, Hq, Hkv, d
+    ("contiguous", False, 1, 13, 2, 1, 8),
+    ("contiguous", False, 4, 9, 2, 2, 16),
+    ("contiguous", True, 4, 7, 4, 2, 8),
+    ("contiguous", True, 8, 5, 4, 1, 4),
+    ("striped", True, 2, 11, 2, 1, 8),
+    ("striped", True, 8, 6, 4, 2, 8),
+    ("striped", False, 4, 5, 3, 1, 4),
+    ("contiguous", True, 2, 16, 6, 3, 32),
+]
+
+
+@pytest.mark.parametrize("layout,causal,P,b,Hq,Hkv,d", RING_CASES)
+def test_ring_equals_dense(layout, causal, P, b, Hq, Hkv, d):
+    rng = np.random.default_rng(P * 100 + b)
+    N = P * b
+    q, k, v = _rand_qkv(rng, N, Hq, Hkv, d, scale=2.0)
+    for u in range(P):
+        tq = ro.shard_positions(layout, u, P, b)
+        o_r, l_r = ro.ring_forward(q[tq], u, k, v, P, layout, causal)
+        o_d, l_d = ro.dense_attention(q[tq], tq, k, v, causal)
+        np.testing.assert_allclose(o_r, o_d, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l_r, l_d, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("layout,causal", [("contiguous", True), ("striped", True),
+                                           ("contiguous", False)])
+def test_order_invariance(layout, causal):
+    rng = np.random.default_rng(7)
+    P, b, Hq, Hkv, d = 8, 6, 4, 2, 8
+    q, k, v = _rand_qkv(rng, P * b, Hq, Hkv, d, scale=3.0)
+    for u in (0, 3, 7):
+        tq = ro.shard_positions(layout, u, P, b)
+        base_o, base_l = ro.ring_forward(q[tq], u, k, v, P, layout, causal)
+        for _ in range(5):
+            order = rng.permutation(P)
+            o, l = ro.ring_forward(q[tq], u, k, v, P, layout, causal, order=order)
+            np.testing.assert_allclose(o, base_o, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(l, base_l, rtol=0, atol=1e-12)
+
+
+def test_p1_is_library_softmax_attention():
+    """P = 1, non-causal: one visit, and the result is softmax(QK^T/sqrt(d)) V
+    computed with scipy's softmax."""
+    rng = np.random.default_rng(11)
+    N, Hq, Hkv, d = 37, 3, 1, 16
+    q, k, v = _rand_qkv(rng, N, Hq, Hkv, d)
+    o, lse = ro.ring_forward(q, 0, k, v, 1, "contiguous", False)
+    for h in range(Hq):
+        s = q[:, h, :] @ k[:, 0, :].T / math.sqrt(d)
+        want = scipy_softmax(s, axis=1) @ v[:, 0, :]
+        np.testing.assert_allclose(o[:, h, :], want, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[h], np.log(np.exp(s).sum(axis=1)), rtol=0, atol=1e-12)
+
+
+def test_causal_library_softmax():
+    """Causal, P = 1: softmax over the lower triangle, via scipy with -inf."""
+    rng = np.random.default_rng(12)
+    N, d = 21, 8
+    q, k, v = _rand_qkv(rng, N, 1, 1, d)
+    o, _ = ro.ring_forward(q, 0, k, v, 1, "contiguous", True)
+    s = q[:, 0, :] @ k[:, 0, :].T / math.sqrt(d)
+    s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+    np.testing.assert_allclose(o[:, 0, :], scipy_softmax(s, axis=1) @ v[:, 0, :], atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and special cases.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout,causal", [("contiguous", True), ("striped", True),
+                                           ("contiguous", False)])
+def test_all_equal_keys_give_mean_of_allowed_values(layout, causal):
+    rng = np.random.default_rng(3)
+    P, b, Hq, Hkv, d = 4, 5, 2, 1, 8
+    N = P * b
+    q = rng.standard_normal((N, Hq, d))
+    key = rng.standard_normal(d)
+    k = np.broadcast_to(key, (N, Hkv, d)).copy()
+    v = rng.standard_normal((N, Hkv, d))
+    for u in range(P):
+        tq = ro.shard_positions(layout, u, P, b)
+        o, lse = ro.ring_forward(q[tq], u, k, v, P, layout, causal)
+        for i, t in enumerate(tq):
+            count = t + 1 if causal else N
+            want = v[:count, 0, :].mean(axis=0)
+            for h in range(Hq):
+                np.testing.assert_allclose(o[i, h], want, rtol=0, atol=1e-12)
+                s0 = q[t, h] @ key / math.sqrt(d)
+                assert abs(lse[h, i] - (s0 + math.log(count))) <= 1e-12
+
+
+def test_dominant_score_returns_that_value_row():
+    rng = np.random.default_rng(5)
+    N, d, P = 16, 4, 4
+    b = N // P
+    q = np.zeros((N, 1, d))
+    q[:, 0, 0] = 1.0
+    k = rng.uniform(-0.5, 0.5, (N, 1, d))
+    k[:, 0, 0] = 0.0
+    star = 9
+    gap = 80.0        # score gap = 80 / sqrt(4) = 40
+    k[star, 0, 0] = gap
+    v = rng.standard_normal((N, 1, d))
+    o, _ = ro.ring_forward(q[0:b], 0, k, v, P, "contiguous", False)
+    s = q[0, 0] @ k[:, 0, :].T / math.sqrt(d)
+    eff_gap = s[star] - np.delete(s, star).max()
+    assert eff_gap >= 39.0
+    bound = (N - 1) * math.exp(-eff_gap) * 2 * np.abs(v).max()
+    assert np.abs(o[0, 0] - v[star, 0]).max() <= bound + 1e-15
+
+
+def test_scale_is_one_over_sqrt_d():
+    """d = 4: q.k1 = 2 so S1 = 1, S2 = 0; O = (e v1 + v2) / (e + 1)."""
+    q = np.ones((1, 1, 4))
+    k = np.zeros((2, 1, 4))
+    k[0, 0, :2] = 1.0
+    v = np.array([[[3.0, -1.0, 0.5, 2.0]], [[-2.0, 4.0, 1.0, 0.0]]])
+    o, lse = ro.dense_attention(q, np.array([1]), k, v, False)
+    e = math.e
+    np.testing.assert_allclose(o[0, 0], (e * v[0, 0] + v[1, 0]) / (e + 1), rtol=0, atol=1e-15)
+    assert abs(lse[0, 0] - math.log(e + 1)) <= 1e-15
+    o2, _ = ro.ring_forward(np.ones((1, 1, 4)), 1, k, v, 2, "contiguous", False)
+    np.testing.assert_allclose(o2[0, 0], o[0, 0], rtol=0, atol=1e-15)
+
+
+def test_causal_predicate_is_inclusive_on_global_positions():
+    rng = np.random.default_rng(8)
+    P, b, d = 4, 3, 4
+    N = P * b
+    q, k, v = _rand_qkv(rng, N, 1, 1, d)
+    # token 0 may only see itself
+    o, lse = ro.ring_forward(q[0:b], 0, k, v, P, "contiguous", True)
+    np.testing.assert_allclose(o[0, 0], v[0, 0], rtol=0, atol=1e-15)
+    assert abs(lse[0, 0] - q[0, 0] @ k[0, 0] / 2.0) <= 1e-15
+    # striped rank 0 row 0 is token 0 as well; rank 3 row 0 is token 3 and sees tokens 0..3
+    o, _ = ro.ring_forward(q[ro.shard_positions("striped", 3, P, b)], 3, k, v, P, "striped", True)
+    o_dense, _ = ro.dense_attention(q[3:4], np.array([3]), k[:4], v[:4], False)
+    np.testing.assert_allclose(o[0, 0], o_dense[0, 0], rtol=0, atol=1e-12)
+
+
+def test_gqa_head_map_contiguous_groups():
+    """Hq = 4, Hkv = 2: heads 0, 1 read key/value head 0 and heads 2, 3 head 1."""
+    rng = np.random.default_rng(9)
+    N, d = 8, 4
+    q = rng.standard_normal((N, 4, d))
+    k = np.zeros((N, 2, d))
+    v = np.zeros((N, 2, d))
+    v[:, 0, :] = 1.0
+    v[:, 1, :] = -5.0
+    o, _ = ro.ring_forward(q[:4], 0, k, v, 2, "contiguous", False)
+    np.testing.assert_allclose(o[:, 0:2, :], 1.0, atol=1e-15, rtol=0)
+    np.testing.assert_allclose(o[:, 2:4, :], -5.0, atol=1e-15, rtol=0)
+
+
+def _brute_force_row(qv, K, V, allowed, d):
+    """Pure Python: weights e^{S_t} without subtracting any maximum, fsum."""
+    ws = [math.exp(sum(a * b for a, b in zip(qv, K[t])) / math.sqrt(d)) for t in allowed]
+    den = math.fsum(ws)
+    out = [math.fsum(w * V[t][c] for w, t in zip(ws, allowed)) / den for c in range(len(V[0]))]
+    return out, math.log(den)
+
+
+@pytest.mark.parametrize("layout,causal,P", [("contiguous", True, 4), ("striped", True, 4),
+                                             ("contiguous", False, 2), ("striped", True, 8)])
+def test_brute_force_tiny(layout, causal, P):
+    rng = np.random.default_rng(13 + P)
+    N, d = 16, 3
+    b = N // P
+    q = rng.uniform(-1, 1, (N, 1, d))
+    k = rng.uniform(-1, 1, (N, 1, d))
+    v = rng.uniform(-1, 1, (N, 1, d))
+    Kl = k[:, 0, :].tolist()
+    Vl = v[:, 0, :].tolist()
+    for u in range(P):
+        # positions written out by hand, independent of shard_positions
+        if layout == "contiguous":
+            tq = list(range(u * b, u * b + b))
+        else:
+            tq = [t for t in range(N) if t % P == u]
+        o, lse = ro.ring_forward(q[tq], u, k, v, P, layout, causal)
+        o_d, lse_d = ro.dense_attention(q[tq], np.array(tq), k, v, causal)
+        for i, t in enumerate(tq):
+            allowed = [s for s in range(N) if (s <= t or not causal)]
+            want, want_lse = _brute_force_row(q[t, 0].tolist(), Kl, Vl, allowed, d)
+            np.testing.assert_allclose(o[i, 0], want, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(o_d[i, 0], want, rtol=0, atol=1e-12)
+            assert abs(lse[0, i] - want_lse) <= 1e-12
+            assert abs(lse_d[0, i] - want_lse) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Layouts and counts.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P,b", [(1, 5), (4, 3), (8, 7)])
+def test_shard_positions(P, b):
+    N = P * b
+    seen = []
+    for r in range(P):
+        c = ro.shard_positions("contiguous", r, P, b)
+        assert c.tolist() == list(range(r * b, (r + 1) * b))
+        s = ro.shard_positions("striped", r, P, b)
+        assert s.tolist() == [t for t in range(N) if t % P == r]
+        seen.extend(s.tolist())
+    assert sorted(seen) == list(range(N))
+
+
+def test_causal_block_counts_match_page():
+    g = _load("causal_block_counts.json")
+    P, b = g["P"], 3
+    counts = []
+    for u in range(P):
+        tq = ro.shard_positions("contiguous", u, P, b)
+        n = sum(bool(ro.allowed_mask(tq, ro.shard_positions("contiguous", r, P, b), True).any())
+                for r in range(P))
+        counts.append(n)
+    assert counts == g["blocks_needed_per_gpu"]
+    assert sum(counts) == g["total_blocks"]
+    assert P * P == g["total_without_mask"]
+
+
+@pytest.mark.parametrize("P,b", [(1, 4), (2, 5), (4, 6), (8, 3)])
+def test_pair_count_closed_forms(P, b):
+    """The closed forms the bench uses for useful FLOPs, against the brute-force mask."""
+    import bench
+    for u in range(P):
+        assert ro.allowed_pair_count("contiguous", u, P, b, True) == \
+            bench.useful_pairs("contiguous", u, P, b, True) == u * b * b + b * (b + 1) // 2
+        assert ro.allowed_pair_count("striped", u, P, b, True) == \
+            bench.useful_pairs("striped", u, P, b, True) == P * b * (b - 1) // 2 + (u + 1) * b
+        assert ro.allowed_pair_count("striped", u, P, b, False) == \
+            bench.useful_pairs("striped", u, P, b, False) == P * b * b
+
+
+def test_bandwidth_budget_figures():
+    """FLOP and byte accounting reproduces the figures printed on the pages."""
+    import bench
+    g = _load("bandwidth_budget.json")
+    f = g["flops_per_block_pair"]
+    got = bench.useful_flops(f["b"] * f["b"], f["d"], 1)
+    assert abs(got / f["printed_flops"] - 1) <= f["printed_rel_precision"]
+    h = g["hop_bytes"]
+    for case in h["cases"]:
+        got = bench.hop_bytes(h["b"], case["d_kv"], 1, h["bytes_per_elem"])
+        assert abs(got / case["printed_bytes"] - 1) <= h["printed_rel_precision"]
+    p = g["per_head_flops_llama70b"]
+    per_head = bench.useful_flops(p["b"] * p["b"], p["d_h"], 1)
+    assert abs(per_head / p["printed_flops_per_head"] - 1) <= p["printed_rel_precision"]
+    all_heads = bench.useful_flops(p["b"] * p["b"], p["d_h"], p["heads"])
+    assert abs(all_heads / p["printed_flops_all_heads"] - 1) <= p["printed_rel_precision"]
+
+
+# ---------------------------------------------------------------------------
+# Merge of partial triples.
+# ---------------------------------------------------------------------------
+
+def _block_partials(q_local, u, k, v, P, layout, causal):
+    """One partial (m, z, y) per visiting block, each folded from the empty state."""
+    b, Hq, d = q_local.shape
+    G = Hq // k.shape[1]
+    tq = ro.shard_positions(layout, u, P, b)
+    ms, zs, ys = [], [], []
+    for r in range(P):
+        tk = ro.shard_positions(layout, r, P, b)
+        allow = ro.allowed_mask(tq, tk, causal)
+        m, z, y = ro.empty_state(b, Hq, d)
+        for h in range(Hq):
+            s = np.where(allow, q_local[:, h, :] @ k[tk, h // G, :].T / math.sqrt(d), -np.inf)
+            m[h], z[h], y[:, h, :] = ro.online_fold(m[h], z[h], y[:, h, :], s, v[tk, h // G, :])
+        ms.append(m)
+        zs.append(z)
+        ys.append(np.transpose(y, (1, 0, 2)))   # [Hq, b, d] to match m, z
+    return np.stack(ms), np.stack(zs), np.stack(ys)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_merge_of_block_partials_equals_dense(layout):
+    rng = np.random.default_rng(21)
+    P, b, Hq, Hkv, d = 4, 6, 2, 1, 8
+    q, k, v = _rand_qkv(rng, P * b, Hq, Hkv, d, scale=2.0)
+    u = 1 if layout == "striped" else 2   # contiguous rank 2 has fully masked blocks 3
+    tq = ro.shard_positions(layout, u, P, b)
+    m, z, y = _block_partials(q[tq], u, k, v, P, layout, True)
+    o, lse = ro.merge_partials(m, z, y)
+    o_d, lse_d = ro.dense_attention(q[tq], tq, k, v, True)
+    np.testing.assert_allclose(np.transpose(o, (1, 0, 2)), o_d, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_d, rtol=0, atol=1e-12)
+
+
+def test_merge_identity_associativity_commutativity():
+    rng = np.random.default_rng(22)
+    n, R, d = 5, 7, 4
+    m = rng.standard_normal((n, R)) * 3
+    z = rng.uniform(0.5, 2.0, (n, R))
+    y = rng.standard_normal((n, R, d))
+    o, lse = ro.merge_partials(m, z, y)
+    # identity: an empty partial (-inf, 0, 0) changes nothing
+    o2, lse2 = ro.merge_partials(np.concatenate([m, np.full((1, R), -np.inf)]),
+                                 np.concatenate([z, np.zeros((1, R))]),
+                                 np.concatenate([y, np.zeros((1, R, d))]))
+    np.testing.assert_allclose(o2, o, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(lse2, lse, atol=1e-14, rtol=0)
+    # commutativity
+    perm = rng.permutation(n)
+    o3, lse3 = ro.merge_partials(m[perm], z[perm], y[perm])
+    np.testing.assert_allclose(o3, o, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(lse3, lse, atol=1e-13, rtol=0)
+    # associativity: a merged pair re-enters as the triple (LSE, 1, O)
+    oa, la = ro.merge_partials(m[:2], z[:2], y[:2])
+    ob, lb = ro.merge_partials(m[2:], z[2:], y[2:])
+    o4, lse4 = ro.merge_partials(np.stack([la, lb]), np.ones((2, R)), np.stack([oa, ob]))
+    np.testing.assert_allclose(o4, o, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(lse4, lse, atol=1e-13, rtol=0)
+    # closed form for two partials with equal maxima: (y1 + y2) / (z1 + z2)
+    mm = np.zeros((2, R))
+    o5, lse5 = ro.merge_partials(mm, z[:2], y[:2])
+    np.testing.assert_allclose(o5, (y[0] + y[1]) / (z[0] + z[1])[:, None], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(lse5, np.log(z[0] + z[1]), atol=1e-14, rtol=0)
+
+
+def test_merge_all_empty():
+    o, lse = ro.merge_partials(np.full((3, 2), -np.inf), np.zeros((3, 2)), np.zeros((3, 2, 4)))
+    assert np.all(o == 0.0)
+    assert np.all(np.isneginf(lse))
+
+
+def test_fold_of_fully_masked_block_keeps_state():
+    m0 = np.array([-np.inf, 1.5])
+    z0 = np.array([0.0, 2.0])
+    y0 = np.array([[0.0, 0.0], [1.0, -1.0]])
+    s = np.full((2, 3), -np.inf)
+    m, z, y = ro.online_fold(m0, z0, y0, s, np.ones((3, 2)))
+    assert np.isneginf(m[0]) and z[0] == 0 and np.all(y[0] == 0)
+    assert m[1] == 1.5 and z[1] == 2.0 and np.all(y[1] == y0[1])
+    assert not np.isnan(np.concatenate([m, z, y.ravel()])).any()
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each plausible error in the oracle must fail some pin.
+# ---------------------------------------------------------------------------
+
+def _fold_without_rescale(m, z, y, s, vals):
+    m_new = np.maximum(m, s.max(axis=1))
+    live = np.isfinite(m_new)
+    m_safe = np.where(live, m_new, 0.0)
+    p = np.where(np.isfinite(s), np.exp(s - m_safe[:, None]), 0.0)
+    return m_new, z + p.sum(axis=1), y + p @ vals
+
+
+def _fold_sign_flipped(m, z, y, s, vals):
+    m_new = np.maximum(m, s.max(axis=1))
+    live = np.isfinite(m_new)
+    m_safe = np.where(live, m_new, 0.0)
+    alpha = np.where(np.isfinite(m), np.exp(m_safe - np.where(np.isfinite(m), m, 0.0)),
+                     np.where(live, 0.0, 1.0))
+    p = np.where(np.isfinite(s), np.exp(s - m_safe[:, None]), 0.0)
+    return m_new, z * alpha + p.sum(axis=1), y * alpha[:, None] + p @ vals
+
+
+_REAL_FOLD = ro.online_fold
+
+
+def _fold_rescale_y_only(m, z, y, s, vals):
+    m_new, z_new, y_new = _REAL_FOLD(m, z, y, s, vals)
+    p_sum = np.where(np.isfinite(s), np.exp(s - np.where(np.isfinite(m_new), m_new, 0)[:, None]), 0).sum(1)
+    return m_new, z + p_sum, y_new          # forgets to rescale z
+
+
+def _exclusive_mask(tq, tk, causal):
+    tq = np.asarray(tq)
+    tk = np.asarray(tk)
+    if not causal:
+        return np.ones((tq.size, tk.size), bool)
+    return tk[None, :] < tq[:, None]
+
+
+def _striped_transposed(layout, r, P, b):
+    j = np.arange(b, dtype=np.int64)
+    if layout == "striped":
+        return r * P + j          # wrong: mixes up local row and shard index
+    return r * b + j
+
+
+def _pins_fail():
+    """Run a representative set of pins; return True if any of them fails."""
+    checks = [test_worked_example_outputs_and_trace, test_p1_is_library_softmax_attention,
+              test_causal_library_softmax, test_scale_is_one_over_sqrt_d,
+              test_causal_predicate_is_inclusive_on_global_positions,
+              test_gqa_head_map_contiguous_groups]
+    checks += [lambda: test_shard_positions(4, 3),
+               lambda: test_brute_force_tiny("striped", True, 4),
+               lambda: test_all_equal_keys_give_mean_of_allowed_values("contiguous", True),
+               lambda: test_ring_equals_dense(*RING_CASES[3])]
+    for c in checks:
+        try:
+            with np.errstate(all="ignore"):
+                c()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("target,replacement", [
+    ("online_fold", _fold_without_rescale),
+    ("online_fold", _fold_sign_flipped),
+    ("online_fold", _fold_rescale_y_only),
+    ("allowed_mask", _exclusive_mask),
+    ("shard_positions", _striped_transposed),
+])
+def test_planted_mistakes_are_caught(monkeypatch, target, replacement):
+    assert not _pins_fail()
+    monkeypatch.setattr(ro, target, replacement)
+    assert _pins_fail(), f"no pin caught a mistake planted in {target}"
+
+
+def test_planted_scale_mistake_is_caught(monkeypatch):
+    real_sqrt = ro.math.sqrt
+
+    class _M:
+        inf = math.inf
+        log = staticmethod(math.log)
+
+        @staticmethod
+        def sqrt(x):
+            return 1.0      # drops the 1/sqrt(d) scale
+
+    assert real_sqrt(4) == 2
+    monkeypatch.setattr(ro, "math", _M)
+    assert _pins_fail()
+
+
+def test_planted_gqa_mistake_is_caught(monkeypatch):
+    real = ro.ring_forward
+
+    def wrong_map(q_local, u, k, v, P, layout, causal, order=None, trace=False):
+        # interleaved head groups instead of contiguous ones
+        Hq, Hkv = q_local.shape[1], k.shape[1]
+        G = Hq // Hkv
+        perm = [(h % Hkv) * G + h // Hkv for h in range(Hq)]
+        res = real(q_local[:, perm, :], u, k, v, P, layout, causal, order, trace)
+        inv = np.argsort(perm)
+        return (res[0][:, inv, :], res[1][inv]) + tuple(res[2:])
+
+    monkeypatch.setattr(ro, "ring_forward", wrong_map)
+    assert _pins_fail()
+
+
+def test_package_exports():
+    assert oracle.ring_forward is ro.ring_forward
+    assert oracle.merge_partials is ro.merge_partials
