@@ -1,9 +1,44 @@
 """Throughput of one device's share of a causal Ring Attention forward pass.
 
-(placeholder: accounting only; the timed path is added with the HIP library)
+One "step" is one call of the whole hot path for rank u: the P ring steps (hop
+copies into the double buffer, the step kernels with the online-softmax fold,
+the fused O/LSE epilogue) over one batch of synthetic input already resident in
+HBM.  Default workload: the million-token share (N = 1,048,576, P = 8, contiguous
+shards, rank 7, 4 query heads / 1 key-value head, d_h = 128, bf16, K scaled by 2,
+causal).
+
+Prints ONE JSON line.  ``value`` is useful (mask-aware) attention TFLOP/s: 4*d_h
+FLOPs per allowed (query, key) pair and query head, divided by the wall time per
+step.  ``roofline`` reports the step kernel against the MI355X bf16 dense MFMA
+peak, with its average launch duration measured by HIP events around every step
+kernel inside the timed region.  ``cpu_baseline`` times the fp64 oracle on the
+host cores on a bounded sample of query rows of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--cpu-seconds S] [--no-cpu-baseline]
 """
+
 from __future__ import annotations
 
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+# MI355X published dense peaks used as roofline denominators.
+PEAK_BF16_TFLOPS = 2516.6     # 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_bf16_traffic.json")
+STEP_SOURCE = os.path.join(ROOT, "ring_attention_block_step_amd", "csrc", "step_bf16.hip")
+
+
+# ---------------------------------------------------------------------------
+# Accounting (pinned against the pages' figures and the oracle's mask counts).
+# ---------------------------------------------------------------------------
 
 def useful_pairs(layout: str, u: int, P: int, b: int, causal: bool) -> int:
     """Allowed (query, key) pairs of rank u over all P visiting blocks, per head.
@@ -34,3 +69,203 @@ def useful_flops(pairs: int, d: int, heads: int) -> float:
 def hop_bytes(b: int, d: int, heads_kv: int, elem_bytes: int) -> int:
     """Bytes of one key/value block on the wire: K and V, b tokens each."""
     return 2 * b * d * heads_kv * elem_bytes
+
+
+def source_digest(path: str = STEP_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per step-kernel launch from committed rocprofv3 counter runs,
+    or None when they are missing or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("step_source_sha256_16") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample of rows.
+# ---------------------------------------------------------------------------
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(w, rank, k_glob, v_glob, seconds: float, gpu_out=None, gpu_lse=None):
+    """Time oracle.dense_attention on growing batches of sampled query rows until
+    about ``seconds`` of work; report useful fp64 TFLOP/s over exactly those rows."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    k = k_glob.double().numpy()
+    v = v_glob.double().numpy()
+    tq_all = oracle.shard_positions(w.layout, rank, w.P, w.b)
+    rows = wl.sample_local_rows(w.b, min(w.b, 4096), w.seed, 0)
+    done, elapsed, flops = 0, 0.0, 0.0
+    batch = 4
+    max_err = mean_err_sum = 0.0
+    n_err = 0
+    while done < rows.size and elapsed < seconds:
+        sel = rows[done:done + batch]
+        tq = tq_all[sel]
+        q = wl.query_rows(w, tq).double().numpy()
+        t0 = time.perf_counter()
+        o, lse = oracle.dense_attention(q, tq, k, v, w.causal)
+        elapsed += time.perf_counter() - t0
+        allowed = (tq + 1) if w.causal else np.full(tq.shape, w.N)
+        flops += 4.0 * w.d * float(allowed.sum()) * w.Hq
+        if gpu_out is not None:
+            err = np.abs(gpu_out[sel].astype(np.float64) - o)
+            max_err = max(max_err, float(err.max()))
+            mean_err_sum += float(err.sum())
+            n_err += err.size
+        done += sel.size
+        batch = min(batch * 2, 256)
+    res = {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": _blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{done} sampled query rows x {w.Hq} heads of rank {rank} "
+                   f"({w.name}); fp64 NumPy dense oracle; {elapsed:.1f} s"),
+    }
+    parity = None
+    if gpu_out is not None and n_err:
+        parity = {"rows": int(done), "max_abs": max_err, "mean_abs": mean_err_sum / n_err}
+    return res, parity
+
+
+# ---------------------------------------------------------------------------
+# Main.
+# ---------------------------------------------------------------------------
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="1m-contiguous-causal")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the path is one device's share of the ring; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import ring_attention_block_step_amd as ra
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 3
+    w = wl.WORKLOADS[args.workload]
+    rank = w.ranks[-1]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_gen = time.perf_counter()
+    k_glob, v_glob = wl.global_kv(w)
+    idx = ra.shard_index(w.N, w.P, w.layout, rank)
+    q = wl.query_rows(w, idx.numpy()).to(dev)
+    k = ra.pack_shards(k_glob, w.P, w.layout).to(dev)
+    v = ra.pack_shards(v_glob, w.P, w.layout).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.Hq, w.b), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s: {w.note}", file=sys.stderr, flush=True)
+
+    def run():
+        ra.forward(q, k, v, P=w.P, rank=rank, causal=w.causal, layout=w.layout, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    ra.timing_collect()
+    ra.timing_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        run()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ra.timing_enable(False)
+    kt = ra.timing_collect()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (host wall {wall:.3f} s)", file=sys.stderr,
+          flush=True)
+
+    pairs = useful_pairs(w.layout, rank, w.P, w.b, w.causal)
+    flops = useful_flops(pairs, w.d, w.Hq)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    launches = kt["step_launches"]
+    avg_launch_ms = kt["step_ms"] / max(1, launches)
+    flops_per_launch = flops * args.steps / max(1, launches)
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12 if launches else None
+    roofline = {
+        "bound": "mfma",
+        "achieved": achieved,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": (achieved / PEAK_BF16_TFLOPS) if achieved else None,
+        "traffic": measured_traffic(w.name),
+        "kernel": "step_bf16_kernel<128>" if w.dtype == "bf16" else "step_f32_kernel",
+        "avg_launch_ms": avg_launch_ms,
+        "launches": launches,
+        "flops_per_launch": flops_per_launch,
+    }
+
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        gpu_out = out.float().cpu().numpy()
+        cpu, parity = cpu_baseline(w, rank, k_glob, v_glob, args.cpu_seconds, gpu_out)
+
+    line = {
+        "metric": "useful attention TFLOP/s per GPU (mask-aware) and % of bf16 MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; Q,K,V as the workload states)",
+        "config": {"workload": w.name, "N": w.N, "P": w.P, "b": w.b, "rank": rank, "layout": w.layout,
+                   "causal": w.causal, "Hq": w.Hq, "Hkv": w.Hkv, "d_h": w.d, "useful_flops": flops},
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

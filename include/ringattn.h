@@ -1,0 +1,134 @@
+/*
+ * ringattn.h -- C ABI of one device's share of a Ring Attention forward pass
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed ("Ring Attention" (aarnphm.xyz), the recurrence for S, m,
+ * z, y and O): device `rank` (u) holds its query block Q^(u) and sees the P
+ * key/value blocks in ring order b(u, s) = (u - s) mod P, s = 0 .. P-1.  Each
+ * visit forms S = Q K^T / sqrt(d_h), folds it into the running per-row
+ * (m, z, y) with the rescale factor exp(m_old - m_new), and after the last
+ * visit O = y / z.  The log-sum-exp LSE = m + ln z (natural log) is written
+ * beside O, the per-row statistics the transformer-math page (aicassindra.com),
+ * section "The backward pass costs a second ring", says are kept.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, on the
+ *    current HIP device, 16-byte aligned, densely packed row-major.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *    stream).  Every call is asynchronous on `stream`: it is ordered after the
+ *    work already on `stream`, and work enqueued later on `stream` sees the
+ *    results.  Inputs must stay alive and unmodified until then.
+ *  - Batch is 1.  Query head h reads key/value head h / (Hq / Hkv).
+ *  - Return value: RINGATTN_OK or an error code.  Argument errors are reported
+ *    before any HIP call is made and nothing is enqueued.  Nothing throws or
+ *    aborts across this ABI.  ringattn_last_error() gives a message for the
+ *    last failure on the calling thread.
+ */
+#ifndef RINGATTN_H
+#define RINGATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  RINGATTN_OK = 0,
+  RINGATTN_EINVAL = 1,       /* bad shape, null pointer, misalignment, out-of-range argument */
+  RINGATTN_EUNSUPPORTED = 2, /* valid but not implemented (e.g. d_h not in {64, 128}) */
+  RINGATTN_EHIP = 3          /* the HIP runtime reported an error (message has the detail) */
+};
+
+enum { RINGATTN_LAYOUT_CONTIGUOUS = 0, RINGATTN_LAYOUT_STRIPED = 1 };
+
+/*
+ * ringattn_forward -- rank `rank`'s share of the ring, bf16 in and out.
+ *
+ * Shard layout (layout): the sequence of N tokens is split into P shards of
+ * b = N / P tokens.  CONTIGUOUS: shard r holds tokens r*b .. r*b+b-1 (the
+ * transformer-math page, "The mechanism, compressed").  STRIPED: token t lives
+ * on shard t mod P, so local row j of shard r is token j*P + r ("Ring
+ * Attention" (aarnphm.xyz): striped ownership balances causal work).
+ * Causal (causal = 1): a query attends to keys at GLOBAL token positions <= its
+ * own ("Ring Attention" (darshanfofadiya.com), 4.8 and 4.8.1).
+ *
+ *  q    [b, Hq, d_h]        bf16, rank's query rows in local order (read only)
+ *  k, v [P, b, Hkv, d_h]    bf16, every shard, shard-major, each in local row
+ *                           order: what the ring would deliver (read only).
+ *                           Shard `rank` is the device's own block.
+ *  out  [b, Hq, d_h]        bf16, O (written)
+ *  lse  [Hq, b]             fp32, natural-log LSE (written), may be NULL
+ *  N, P, rank               N % P == 0, N >= P >= 1, 0 <= rank < P
+ *  Hq, Hkv                  Hq % Hkv == 0
+ *  d_h                      64 or 128
+ *  causal                   0 or 1
+ *  layout                   RINGATTN_LAYOUT_CONTIGUOUS or _STRIPED
+ *
+ * The library allocates its workspace (two key/value slots and the fp32 running
+ * state) stream-ordered on `stream` and frees it the same way.  The block for
+ * step s+1 is copied into the free slot on a second, library-owned stream while
+ * step s computes: the one-GPU stand-in for the ring hop.
+ */
+int ringattn_forward(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t N, int P, int rank, int Hq, int Hkv, int d_h,
+                     int causal, int layout, void* stream);
+
+/* ringattn_forward_f32 -- identical to ringattn_forward with fp32 q, k, v and
+ * out; every quantity is computed in fp32. */
+int ringattn_forward_f32(const float* q, const float* k, const float* v, float* out, float* lse,
+                         int64_t N, int P, int rank, int Hq, int Hkv, int d_h,
+                         int causal, int layout, void* stream);
+
+/*
+ * ringattn_merge -- combine `nparts` partial (m, z, y) triples of the same
+ * rows with one rescale-and-add (the transformer-math page, "The ring is a
+ * prefill algorithm": each shard returns a partial (m, l, o) and one small
+ * reduction combines them).  m* = max_i m_i, w_i = exp(m_i - m*),
+ * O = sum_i w_i y_i / sum_i w_i z_i, LSE = m* + ln sum_i w_i z_i.
+ *
+ *  m, z  [nparts, Hq, rows]       fp32; m in natural-log units, z >= 0
+ *  y     [nparts, rows, Hq, d_h]  fp32, unnormalised
+ *  out   [rows, Hq, d_h]          out_dtype: 0 = bf16, 1 = fp32 (written)
+ *  lse   [Hq, rows]               fp32 (written), may be NULL
+ *  A partial with m = -inf, z = 0 contributes nothing; a row whose partials
+ *  are all empty gets O = 0 and LSE = -inf.  nparts >= 1, rows >= 0, Hq >= 1,
+ *  d_h in {64, 128}.
+ */
+int ringattn_merge(const float* m, const float* z, const float* y, int nparts,
+                   int64_t rows, int Hq, int d_h, void* out, int out_dtype,
+                   float* lse, void* stream);
+
+/* Static string for a status code. */
+const char* ringattn_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* ringattn_last_error(void);
+
+/*
+ * Kernel timing for measurement.  While enabled (enable = 1) every step kernel
+ * that ringattn_forward / ringattn_forward_f32 launches, and every merge
+ * kernel, is bracketed by a pair of HIP events on the stream it runs on.
+ * ringattn_timing_collect() waits for the recorded events, returns the summed
+ * duration (ms) and count of the step kernels and of the merge kernels since
+ * the last collect, and releases the events.  Returns a status code.
+ */
+int ringattn_timing_enable(int enable);
+int ringattn_timing_collect(double* step_ms, int64_t* step_launches,
+                            double* merge_ms, int64_t* merge_launches);
+
+/*
+ * Debug switch: when serial = 1 every key/value hop copy runs on the caller's
+ * stream instead of the library's second stream (no overlap).  Results are
+ * bit-identical either way; used to test the double buffer for races.
+ */
+int ringattn_set_serial_hops(int serial);
+
+/* Library version, e.g. "ringattn 0.1.0 gfx950". */
+const char* ringattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGATTN_H */

@@ -1,0 +1,209 @@
+"""One device's share of a Ring Attention forward pass on MI355X (gfx950).
+
+Python binding of ``libringattn.so`` (C ABI: ``include/ringattn.h``).  It only
+marshals arguments: it checks torch tensors, passes their device pointers and
+the current HIP stream, and raises on a non-zero status.  Every step of the
+computation runs in the library's HIP kernels; there is no CPU or PyTorch
+fallback, and using any entry point without the built library raises.
+
+Names follow the C ABI: ``forward`` (``ringattn_forward`` for bf16,
+``ringattn_forward_f32`` for fp32), ``merge`` (``ringattn_merge``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["forward", "merge", "shard_index", "pack_shards", "lib", "RingAttnError",
+           "timing_enable", "timing_collect", "set_serial_hops", "version", "SYMBOLS", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
+LAYOUTS = {"contiguous": 0, "striped": 1}
+
+# Every symbol include/ringattn.h declares.
+SYMBOLS = ("ringattn_forward", "ringattn_forward_f32", "ringattn_merge", "ringattn_status_string",
+           "ringattn_last_error", "ringattn_timing_enable", "ringattn_timing_collect",
+           "ringattn_set_serial_hops", "ringattn_version")
+
+_lib = None
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m ring_attention_block_step_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    fwd = [vp, vp, vp, vp, f32p, i64, i32, i32, i32, i32, i32, i32, i32, vp]
+    L.ringattn_forward.argtypes = fwd
+    L.ringattn_forward.restype = i32
+    L.ringattn_forward_f32.argtypes = fwd
+    L.ringattn_forward_f32.restype = i32
+    L.ringattn_merge.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, i32, f32p, vp]
+    L.ringattn_merge.restype = i32
+    L.ringattn_status_string.argtypes = [i32]
+    L.ringattn_status_string.restype = ctypes.c_char_p
+    L.ringattn_last_error.argtypes = []
+    L.ringattn_last_error.restype = ctypes.c_char_p
+    L.ringattn_timing_enable.argtypes = [i32]
+    L.ringattn_timing_enable.restype = i32
+    L.ringattn_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.ringattn_timing_collect.restype = i32
+    L.ringattn_set_serial_hops.argtypes = [i32]
+    L.ringattn_set_serial_hops.restype = i32
+    L.ringattn_version.argtypes = []
+    L.ringattn_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        L = lib()
+        raise RingAttnError(rc, f"{L.ringattn_status_string(rc).decode()}: {L.ringattn_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+# ---------------------------------------------------------------------------
+# Caller-side data arrangement (not part of the step; plain torch indexing).
+# ---------------------------------------------------------------------------
+
+def shard_index(N: int, P: int, layout: str, r: int) -> torch.Tensor:
+    """Global token indices held by shard r, in its local row order."""
+    _need(N % P == 0, "N must be a multiple of P")
+    b = N // P
+    grid = torch.arange(N, dtype=torch.int64)
+    if layout == "contiguous":
+        return grid.view(P, b)[r].clone()
+    if layout == "striped":
+        return grid.view(b, P)[:, r].clone()
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def pack_shards(x: torch.Tensor, P: int, layout: str) -> torch.Tensor:
+    """[N, ...] in global token order -> [P, N/P, ...] shard-major, contiguous."""
+    N = x.shape[0]
+    _need(N % P == 0, "N must be a multiple of P")
+    b = N // P
+    if layout == "contiguous":
+        return x.reshape(P, b, *x.shape[1:]).contiguous()
+    if layout == "striped":
+        return x.reshape(b, P, *x.shape[1:]).transpose(0, 1).contiguous()
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+# ---------------------------------------------------------------------------
+# Entry points.
+# ---------------------------------------------------------------------------
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, rank: int, causal: bool,
+            layout: str = "contiguous", out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+            want_lse: bool = True):
+    """Rank ``rank``'s share of the ring.
+
+    q: [b, Hq, d] and k, v: [P, b, Hkv, d] on one HIP device, all bf16 or all
+    fp32, contiguous.  Returns (out [b, Hq, d] in the input dtype, lse [Hq, b]
+    fp32 natural log, or None when want_lse is False and no lse is given).
+    Asynchronous on the current stream of q's device.
+    """
+    L = lib()
+    _need(q.is_cuda and k.is_cuda and v.is_cuda, "q, k, v must be device tensors")
+    _need(q.device == k.device == v.device, "q, k, v must be on one device")
+    _need(q.dtype == k.dtype == v.dtype and q.dtype in (torch.bfloat16, torch.float32),
+          "q, k, v must all be bfloat16 or all float32")
+    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
+    _need(q.dim() == 3 and k.dim() == 4 and v.shape == k.shape, "q [b, Hq, d], k and v [P, b, Hkv, d]")
+    b, Hq, d = q.shape
+    _need(k.shape[0] == P and k.shape[1] == b and k.shape[3] == d, "k, v must be [P, b, Hkv, d] matching q")
+    Hkv = k.shape[2]
+    _need(layout in LAYOUTS, f"layout must be one of {sorted(LAYOUTS)}")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous() and out.device == q.device,
+          "out must match q")
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, b), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse.shape == (Hq, b) and lse.dtype == torch.float32 and lse.is_contiguous()
+              and lse.device == q.device, "lse must be float32 [Hq, b] on q's device")
+    fn = L.ringattn_forward if q.dtype == torch.bfloat16 else L.ringattn_forward_f32
+    with torch.cuda.device(q.device):
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), P * b, P, rank, Hq, Hkv, d,
+                  int(bool(causal)), LAYOUTS[layout], _stream(q.device)))
+    return out, lse
+
+
+def merge(m: torch.Tensor, z: torch.Tensor, y: torch.Tensor, *, out_dtype=torch.bfloat16,
+          out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Combine partial triples: m, z [n, Hq, rows], y [n, rows, Hq, d], fp32.
+
+    Returns (out [rows, Hq, d] in out_dtype, lse [Hq, rows] fp32 or None).
+    """
+    L = lib()
+    _need(m.is_cuda and z.is_cuda and y.is_cuda and m.device == z.device == y.device,
+          "m, z, y must be on one device")
+    _need(m.dtype == z.dtype == y.dtype == torch.float32, "m, z, y must be float32")
+    _need(m.is_contiguous() and z.is_contiguous() and y.is_contiguous(), "m, z, y must be contiguous")
+    _need(m.dim() == 3 and z.shape == m.shape and y.dim() == 4, "m, z [n, Hq, rows]; y [n, rows, Hq, d]")
+    n, Hq, rows = m.shape
+    _need(y.shape[0] == n and y.shape[1] == rows and y.shape[2] == Hq, "y must be [n, rows, Hq, d]")
+    d = y.shape[3]
+    _need(out_dtype in (torch.bfloat16, torch.float32), "out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((rows, Hq, d), dtype=out_dtype, device=m.device)
+    _need(out.shape == (rows, Hq, d) and out.dtype == out_dtype and out.is_contiguous()
+          and out.device == m.device, "out must be [rows, Hq, d] of out_dtype")
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, rows), dtype=torch.float32, device=m.device)
+    if lse is not None:
+        _need(lse.shape == (Hq, rows) and lse.dtype == torch.float32 and lse.is_contiguous()
+              and lse.device == m.device, "lse must be float32 [Hq, rows]")
+    with torch.cuda.device(m.device):
+        _check(L.ringattn_merge(_ptr(m), _ptr(z), _ptr(y), n, rows, Hq, d, _ptr(out),
+                                0 if out_dtype == torch.bfloat16 else 1, _ptr(lse), _stream(m.device)))
+    return out, lse
+
+
+def timing_enable(flag: bool = True) -> None:
+    _check(lib().ringattn_timing_enable(int(bool(flag))))
+
+
+def timing_collect() -> dict:
+    """Summed kernel durations (ms) and launch counts since the last collect."""
+    sm, mm = ctypes.c_double(), ctypes.c_double()
+    sn, mn = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ringattn_timing_collect(ctypes.byref(sm), ctypes.byref(sn), ctypes.byref(mm), ctypes.byref(mn)))
+    return {"step_ms": sm.value, "step_launches": sn.value, "merge_ms": mm.value, "merge_launches": mn.value}
+
+
+def set_serial_hops(flag: bool) -> None:
+    _check(lib().ringattn_set_serial_hops(int(bool(flag))))
+
+
+def version() -> str:
+    return lib().ringattn_version().decode()

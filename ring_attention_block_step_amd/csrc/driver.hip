@@ -1,0 +1,390 @@
+// Host side of the C ABI: argument checks, the ring-step loop, the double
+// buffer with its copy stream, workspace, timing.  No exception or abort
+// crosses the ABI: every failure becomes a status code plus a thread-local
+// message.
+//
+// The step loop ("Ring Attention" (aarnphm.xyz): at step s device u folds in
+// shard b(u, s) = (u - s) mod p; "Ring Attention: distributed attention across
+// devices" (aicomputerinstitute.com), section "The ring: keep queries still,
+// rotate keys and values": the next block is received while the current one is
+// computed):
+//
+//   slot[0] <- own shard                      (caller stream, before step 0)
+//   slot[1] <- shard of step 1                (copy stream)
+//   for each computed step i:
+//     caller stream waits "slot i%2 filled";  step kernel on slot i%2
+//     if a step i+2 exists: copy stream waits "step i done",
+//                           slot i%2 <- shard of step i+2, signals "filled"
+//
+// Blocks that a causal mask hides completely (contiguous shards, r > rank) are
+// neither copied nor launched; the first computed step starts from the empty
+// state and the last one writes O and LSE.
+#include <mutex>
+#include <string>
+#include <vector>
+#include <cmath>
+#include <cstdio>
+#include <cstdarg>
+
+#include "../../include/ringattn.h"
+#include "internal.h"
+
+using namespace ringattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(RINGATTN_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceCtx {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t hop = nullptr;
+  hipEvent_t ev_start = nullptr;
+  hipEvent_t ev_ready[2] = {nullptr, nullptr};
+  hipEvent_t ev_done[2] = {nullptr, nullptr};
+};
+DeviceCtx g_dev[kMaxDevices];
+
+struct TimedLaunch {
+  hipEvent_t begin, end;
+  int kind;  // 0 step, 1 merge
+};
+std::mutex g_timing_mu;
+bool g_timing = false;
+std::vector<TimedLaunch> g_timed;
+
+bool g_serial_hops = false;
+
+int device_ctx(DeviceCtx** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RINGATTN_EUNSUPPORTED, "device index %d out of range", dev);
+  DeviceCtx& c = g_dev[dev];
+  std::lock_guard<std::mutex> lk(c.mu);
+  if (!c.ready) {
+    HIP_TRY(hipStreamCreateWithFlags(&c.hop, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreateWithFlags(&c.ev_start, hipEventDisableTiming));
+    for (int i = 0; i < 2; ++i) {
+      HIP_TRY(hipEventCreateWithFlags(&c.ev_ready[i], hipEventDisableTiming));
+      HIP_TRY(hipEventCreateWithFlags(&c.ev_done[i], hipEventDisableTiming));
+    }
+    // Keep freed stream-ordered workspace in the pool between calls.
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+      uint64_t thr = UINT64_MAX;
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    }
+    (void)hipGetLastError();
+    c.ready = true;
+  }
+  *out = &c;
+  return RINGATTN_OK;
+}
+
+// Records a begin event before a kernel when timing is on; returns its index or -1.
+int timing_begin(hipStream_t st, int kind) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!g_timing) return -1;
+  TimedLaunch t{nullptr, nullptr, kind};
+  if (hipEventCreate(&t.begin) != hipSuccess || hipEventCreate(&t.end) != hipSuccess) return -1;
+  if (hipEventRecord(t.begin, st) != hipSuccess) return -1;
+  g_timed.push_back(t);
+  return (int)g_timed.size() - 1;
+}
+
+void timing_end(int idx, hipStream_t st) {
+  if (idx < 0) return;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (idx < (int)g_timed.size()) (void)hipEventRecord(g_timed[idx].end, st);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Mask of visiting block r for rank u; returns false if the block is fully masked.
+bool block_mask(int causal, int layout, int r, int u, int* shift) {
+  if (!causal) {
+    *shift = kMaskNone;
+    return true;
+  }
+  if (layout == RINGATTN_LAYOUT_CONTIGUOUS) {
+    if (r < u) { *shift = kMaskNone; return true; }
+    if (r == u) { *shift = 0; return true; }
+    return false;
+  }
+  *shift = (r <= u) ? 0 : 1;
+  return true;
+}
+
+int check_forward_args(const void* q, const void* k, const void* v, const void* out, const void* lse, int64_t N,
+                       int P, int rank, int Hq, int Hkv, int d_h, int causal, int layout) {
+  if (!q || !k || !v || !out) return fail(RINGATTN_EINVAL, "q, k, v and out must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)))
+    return fail(RINGATTN_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (P < 1) return fail(RINGATTN_EINVAL, "P must be >= 1 (got %d)", P);
+  if (N < P) return fail(RINGATTN_EINVAL, "N must be >= P (got N=%lld, P=%d)", (long long)N, P);
+  if (N % P != 0) return fail(RINGATTN_EINVAL, "N (%lld) must be a multiple of P (%d)", (long long)N, P);
+  if (rank < 0 || rank >= P) return fail(RINGATTN_EINVAL, "rank %d outside [0, %d)", rank, P);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(RINGATTN_EINVAL, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (got %d, %d)", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(RINGATTN_EINVAL, "causal must be 0 or 1");
+  if (layout != RINGATTN_LAYOUT_CONTIGUOUS && layout != RINGATTN_LAYOUT_STRIPED)
+    return fail(RINGATTN_EINVAL, "layout must be 0 (contiguous) or 1 (striped)");
+  if (d_h != 64 && d_h != 128) return fail(RINGATTN_EUNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
+  const int64_t b = N / P;
+  if (b > (int64_t)1 << 28 || (int64_t)Hq * b > ((int64_t)1 << 31) / 64)
+    return fail(RINGATTN_EUNSUPPORTED, "shard too large (b=%lld, Hq=%d)", (long long)b, Hq);
+  return RINGATTN_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+template <typename StepFn, typename HopFn>
+int run_ring(int P, int rank, int causal, int layout, size_t slot_bytes, size_t carry_bytes, hipStream_t st,
+             HopFn hop_into, StepFn step) {
+  DeviceCtx* ctx = nullptr;
+  int rc = device_ctx(&ctx);
+  if (rc != RINGATTN_OK) return rc;
+
+  struct Visit { int r, shift; };
+  std::vector<Visit> visits;
+  for (int s = 0; s < P; ++s) {
+    const int r = ((rank - s) % P + P) % P;
+    int shift;
+    if (block_mask(causal, layout, r, rank, &shift)) visits.push_back({r, shift});
+  }
+  const int n = (int)visits.size();  // >= 1: the own block is never fully masked
+
+  std::lock_guard<std::mutex> lk(ctx->mu);
+  const bool serial = g_serial_hops;
+  hipStream_t hs = serial ? st : ctx->hop;
+
+  void* ws = nullptr;
+  HIP_TRY(hipMallocAsync(&ws, 2 * slot_bytes + carry_bytes, st));
+  char* slot[2] = {static_cast<char*>(ws), static_cast<char*>(ws) + slot_bytes};
+  char* carry = static_cast<char*>(ws) + 2 * slot_bytes;
+
+  int status = RINGATTN_OK;
+  auto run = [&]() -> int {
+    if (!serial) {
+      HIP_TRY(hipEventRecord(ctx->ev_start, st));
+      HIP_TRY(hipStreamWaitEvent(hs, ctx->ev_start, 0));
+    }
+    HIP_TRY(hop_into(visits[0].r, slot[0], st));
+    if (n > 1) {
+      HIP_TRY(hop_into(visits[1].r, slot[1], hs));
+      if (!serial) HIP_TRY(hipEventRecord(ctx->ev_ready[1], hs));
+    }
+    for (int i = 0; i < n; ++i) {
+      if (i > 0 && !serial) HIP_TRY(hipStreamWaitEvent(st, ctx->ev_ready[i & 1], 0));
+      const int tix = timing_begin(st, 0);
+      HIP_TRY(step(slot[i & 1], carry, visits[i].shift, i > 0, i == n - 1, st));
+      timing_end(tix, st);
+      if (i + 2 < n) {
+        if (!serial) {
+          HIP_TRY(hipEventRecord(ctx->ev_done[i & 1], st));
+          HIP_TRY(hipStreamWaitEvent(hs, ctx->ev_done[i & 1], 0));
+        }
+        HIP_TRY(hop_into(visits[i + 2].r, slot[i & 1], hs));
+        if (!serial) HIP_TRY(hipEventRecord(ctx->ev_ready[i & 1], hs));
+      }
+    }
+    return RINGATTN_OK;
+  };
+  status = run();
+  // Every copy-stream operation was waited on by the caller stream before its
+  // slot was read, so freeing on the caller stream is ordered after all of them.
+  hipError_t fe = hipFreeAsync(ws, st);
+  if (status == RINGATTN_OK && fe != hipSuccess)
+    return fail(RINGATTN_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+  return status;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ringattn_forward(const void* q, const void* k, const void* v, void* out, float* lse, int64_t N, int P, int rank,
+                     int Hq, int Hkv, int d_h, int causal, int layout, void* stream) {
+  int rc = check_forward_args(q, k, v, out, lse, N, P, rank, Hq, Hkv, d_h, causal, layout);
+  if (rc != RINGATTN_OK) return rc;
+  const int b = (int)(N / P);
+  const int D = d_h;
+  const int G = Hq / Hkv;
+  const int bpad = (int)padded_rows(b);
+  const int npb = bpad / kWaveRows;
+  const size_t kv_elems = (size_t)Hkv * bpad * D;
+  const size_t slot_bytes = round_up(2 * kv_elems * sizeof(__bf16), 256);
+  const size_t cy_bytes = round_up((size_t)Hq * bpad * D * sizeof(float), 256);
+  const size_t cmz_bytes = round_up((size_t)Hq * bpad * 2 * sizeof(float), 256);
+  const size_t carry_bytes = cy_bytes + 2 * cmz_bytes;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const __bf16* kb = static_cast<const __bf16*>(k);
+  const __bf16* vb = static_cast<const __bf16*>(v);
+  const size_t shard_elems = (size_t)b * Hkv * D;
+
+  auto hop = [&](int r, char* slot, hipStream_t s) -> hipError_t {
+    __bf16* kp = reinterpret_cast<__bf16*>(slot);
+    return launch_pack_bf16(kb + (size_t)r * shard_elems, vb + (size_t)r * shard_elems, kp, kp + kv_elems, b,
+                            bpad, Hkv, D, s);
+  };
+  auto step = [&](char* slot, char* carry, int shift, bool carry_in, bool last, hipStream_t s) -> hipError_t {
+    StepBf16Args a;
+    a.q = static_cast<const __bf16*>(q);
+    a.kp = reinterpret_cast<const __bf16*>(slot);
+    a.vp = a.kp + kv_elems;
+    a.cy = reinterpret_cast<float*>(carry);
+    a.cm = reinterpret_cast<float*>(carry + cy_bytes);
+    a.cz = reinterpret_cast<float*>(carry + cy_bytes + cmz_bytes);
+    a.out = static_cast<__bf16*>(out);
+    a.lse = lse;
+    a.b = b;
+    a.bpad = bpad;
+    a.npb = npb;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.items = G * npb;
+    a.wgs_per_head = (a.items + kStepWaves - 1) / kStepWaves;
+    a.shift = shift;
+    a.carry_in = carry_in;
+    a.last = last;
+    a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+    return launch_step_bf16(a, D, s);
+  };
+  return run_ring(P, rank, causal, layout, slot_bytes, carry_bytes, st, hop, step);
+}
+
+int ringattn_forward_f32(const float* q, const float* k, const float* v, float* out, float* lse, int64_t N, int P,
+                         int rank, int Hq, int Hkv, int d_h, int causal, int layout, void* stream) {
+  int rc = check_forward_args(q, k, v, out, lse, N, P, rank, Hq, Hkv, d_h, causal, layout);
+  if (rc != RINGATTN_OK) return rc;
+  const int b = (int)(N / P);
+  const int D = d_h;
+  const size_t shard_elems = (size_t)b * Hkv * D;
+  const size_t half = round_up(shard_elems * sizeof(float), 256);
+  const size_t slot_bytes = 2 * half;
+  const size_t cmz = round_up((size_t)Hq * b * sizeof(float), 256);
+  const size_t carry_bytes = 2 * cmz + round_up((size_t)Hq * b * D * sizeof(float), 256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  auto hop = [&](int r, char* slot, hipStream_t s) -> hipError_t {
+    hipError_t e = hipMemcpyAsync(slot, k + (size_t)r * shard_elems, shard_elems * sizeof(float),
+                                  hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+    return hipMemcpyAsync(slot + half, v + (size_t)r * shard_elems, shard_elems * sizeof(float),
+                          hipMemcpyDeviceToDevice, s);
+  };
+  auto step = [&](char* slot, char* carry, int shift, bool carry_in, bool last, hipStream_t s) -> hipError_t {
+    StepF32Args a;
+    a.q = q;
+    a.k = reinterpret_cast<const float*>(slot);
+    a.v = reinterpret_cast<const float*>(slot + half);
+    a.cm = reinterpret_cast<float*>(carry);
+    a.cz = reinterpret_cast<float*>(carry + cmz);
+    a.cy = reinterpret_cast<float*>(carry + 2 * cmz);
+    a.out = out;
+    a.lse = lse;
+    a.b = b;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.shift = shift;
+    a.carry_in = carry_in;
+    a.last = last;
+    a.scale = (float)(1.0 / std::sqrt((double)D));
+    return launch_step_f32(a, D, s);
+  };
+  return run_ring(P, rank, causal, layout, slot_bytes, carry_bytes, st, hop, step);
+}
+
+int ringattn_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows, int Hq, int d_h,
+                   void* out, int out_dtype, float* lse, void* stream) {
+  if (!m || !z || !y || !out) return fail(RINGATTN_EINVAL, "m, z, y and out must be non-null");
+  if (!aligned16(y) || !aligned16(out) || !aligned16(m) || !aligned16(z) || (lse && !aligned16(lse)))
+    return fail(RINGATTN_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (nparts < 1) return fail(RINGATTN_EINVAL, "nparts must be >= 1");
+  if (rows < 0) return fail(RINGATTN_EINVAL, "rows must be >= 0");
+  if (Hq < 1) return fail(RINGATTN_EINVAL, "Hq must be >= 1");
+  if (out_dtype != 0 && out_dtype != 1) return fail(RINGATTN_EINVAL, "out_dtype must be 0 (bf16) or 1 (fp32)");
+  if (d_h != 64 && d_h != 128) return fail(RINGATTN_EUNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
+  if (rows * (int64_t)Hq > ((int64_t)1 << 31) / 2) return fail(RINGATTN_EUNSUPPORTED, "too many rows");
+  if (rows == 0) return RINGATTN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int tix = timing_begin(st, 1);
+  HIP_TRY(launch_merge(m, z, y, nparts, rows, Hq, d_h, out, out_dtype, lse, st));
+  timing_end(tix, st);
+  return RINGATTN_OK;
+}
+
+const char* ringattn_status_string(int status) {
+  switch (status) {
+    case RINGATTN_OK: return "ok";
+    case RINGATTN_EINVAL: return "invalid argument";
+    case RINGATTN_EUNSUPPORTED: return "unsupported";
+    case RINGATTN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ringattn_last_error(void) { return g_last_error.c_str(); }
+
+int ringattn_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing = enable != 0;
+  return RINGATTN_OK;
+}
+
+int ringattn_timing_collect(double* step_ms, int64_t* step_launches, double* merge_ms, int64_t* merge_launches) {
+  std::vector<TimedLaunch> taken;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    taken.swap(g_timed);
+  }
+  double sums[2] = {0.0, 0.0};
+  int64_t counts[2] = {0, 0};
+  int status = RINGATTN_OK;
+  for (auto& t : taken) {
+    float ms = 0.f;
+    if (status == RINGATTN_OK) {
+      hipError_t e = hipEventSynchronize(t.end);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.begin, t.end);
+      if (e != hipSuccess) status = fail(RINGATTN_EHIP, "timing events: %s", hipGetErrorString(e));
+    }
+    sums[t.kind] += ms;
+    counts[t.kind] += 1;
+    (void)hipEventDestroy(t.begin);
+    (void)hipEventDestroy(t.end);
+  }
+  if (step_ms) *step_ms = sums[0];
+  if (step_launches) *step_launches = counts[0];
+  if (merge_ms) *merge_ms = sums[1];
+  if (merge_launches) *merge_launches = counts[1];
+  return status;
+}
+
+int ringattn_set_serial_hops(int serial) {
+  g_serial_hops = serial != 0;
+  return RINGATTN_OK;
+}
+
+const char* ringattn_version(void) { return "ringattn 0.1.0 gfx950"; }
+
+}  // extern "C"

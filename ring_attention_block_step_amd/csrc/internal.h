@@ -1,0 +1,81 @@
+// Internal declarations shared by the host driver and the kernel files.
+// Not part of the public ABI (include/ringattn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ringattn {
+
+// Key tile of the bf16 step kernel, and the query rows one wavefront owns.
+constexpr int kKeyTile = 64;
+constexpr int kWaveRows = 64;
+constexpr int kStepWaves = 4;
+
+// Mask of one visiting block, in LOCAL row indices (query row i, key row j):
+//   kMaskNone   every key row j < b is allowed;
+//   shift 0     allowed iff j <= i;
+//   shift 1     allowed iff j <  i.
+// Contiguous causal shards give "none" for earlier blocks and shift 0 for the
+// own block (later blocks are fully masked and never launched); striped causal
+// shards give shift 0 for blocks r <= rank and shift 1 for r > rank.
+constexpr int kMaskNone = -1;
+
+struct StepBf16Args {
+  const __bf16* q;   // [b, Hq, D] caller's query rows
+  const __bf16* kp;  // slot keys   [Hkv][bpad/64] tiles of 64 x D, swizzled (key_tile_off)
+  const __bf16* vp;  // slot values [Hkv][bpad/64] tiles of D x 64, transposed, swizzled (val_tile_off)
+  float* cy;         // running y   [Hq*npb][2][D/32][16][64]  (register order)
+  float* cm;         // running m   [Hq*npb][2][64]  (log2 units, scaled)
+  float* cz;         // running z   [Hq*npb][2][64]  (per-lane partial sums)
+  __bf16* out;       // [b, Hq, D]
+  float* lse;        // [Hq, b] or null
+  int b, bpad, npb, Hq, Hkv, G;
+  int items;         // query items per key/value head: G * npb
+  int wgs_per_head;  // ceil(items / kStepWaves)
+  int shift;         // kMaskNone, 0 or 1
+  int carry_in;      // read the running state instead of starting empty
+  int last;          // finish: write O and LSE instead of the running state
+  float sl2;         // log2(e) / sqrt(D)
+};
+
+struct StepF32Args {
+  const float* q;    // [b, Hq, D]
+  const float* k;    // slot [b, Hkv, D]
+  const float* v;    // slot [b, Hkv, D]
+  float* cm;         // [Hq, b] natural-log units
+  float* cz;         // [Hq, b]
+  float* cy;         // [Hq, b, D]
+  float* out;        // [b, Hq, D]
+  float* lse;        // [Hq, b] or null
+  int b, Hq, Hkv, G;
+  int shift, carry_in, last;
+  float scale;       // 1 / sqrt(D)
+};
+
+// Byte offset of 16-byte chunk `chunk` of row `row` inside one 64-key tile of a
+// slot, which is also its LDS image (tiles are copied to LDS verbatim).
+//  key tile:   64 rows (keys) x D bf16; row = 2*D bytes.
+//  value tile: D rows (d) x 64 keys bf16 (keys permuted in groups of 16); row = 128 bytes.
+// Chunks are XOR-swizzled so that the 32 lanes of a wave reading one chunk
+// column of 32 consecutive rows (the MFMA A-operand read) hit distinct banks.
+__host__ __device__ inline int key_tile_off(int D, int row, int chunk) {
+  return D == 128 ? row * 256 + ((chunk ^ (row & 15)) << 4) : row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+__host__ __device__ inline int val_tile_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// Round b up to whole key tiles.
+inline int64_t padded_rows(int64_t b) { return (b + kKeyTile - 1) / kKeyTile * kKeyTile; }
+
+// Ring hop stand-in for bf16: copy shard (k_shard, v_shard: [b, Hkv, D]) into a
+// slot in the step kernel's layout (keys row-major per head, values transposed
+// per 64-key tile), zero-filling rows b .. bpad-1.
+hipError_t launch_pack_bf16(const __bf16* k_shard, const __bf16* v_shard, __bf16* kp, __bf16* vp,
+                            int b, int bpad, int Hkv, int D, hipStream_t st);
+
+hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st);
+hipError_t launch_step_f32(const StepF32Args& a, int D, hipStream_t st);
+hipError_t launch_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows,
+                        int Hq, int D, void* out, int out_f32, float* lse, hipStream_t st);
+
+}  // namespace ringattn

@@ -1,0 +1,397 @@
+// One ring step on bf16 inputs: the visiting key/value block is folded into the
+// running (m, z, y) of every local query row ("Ring Attention" (aarnphm.xyz),
+// the recurrence for S, m, z, y; O = y / z after the last visit).
+//
+// Formulation.  Each wavefront owns 64 query rows of one query head and keeps
+// everything per query in the SAME lane across both contractions:
+//   S^T = K Q^T     A = key tile rows from LDS, B = the wave's query rows
+//                   (held in registers for the whole launch);
+//   O^T += V^T P^T  A = transposed value tile from LDS, B = the probability
+//                   registers produced by the softmax, unmoved.
+// With v_mfma_f32_32x32x16_bf16 the accumulator of a 32x32 tile gives lane l
+// column l % 32 (a query) and 16 rows (keys, or d-rows of O^T), so the row
+// statistics of a query live in two lanes (l and l ^ 32) and the rescale of O
+// by exp(m_old - m_new) is a per-lane multiply.
+//
+// Workgroup: 4 waves (one per SIMD) = 4 query items (query head, 64 rows) that
+// share one key/value head, so every key/value tile staged in LDS serves 256
+// queries.  Tiles of 64 keys move global -> LDS with direct-to-LDS loads
+// (global_load_lds_dwordx4), double-buffered; the slot layout already is the
+// swizzled LDS image.
+//
+// Software pipeline over the tiles every row of the workgroup sees in full:
+// iteration t issues the MFMAs of S(t+1) while the VALU computes the
+// probabilities of tile t, then the MFMAs of PV(t) while the VALU reduces the
+// row maxima of S(t+1).  Tiles that need an element mask (the causal diagonal,
+// the ragged tail) run afterwards without the pipeline.
+//
+// Softmax in base 2: scores are scaled by log2(e)/sqrt(d) inside one FMA, and
+// m is kept in those units.  The running reference m is raised only when a
+// tile's maximum exceeds it by more than kLazy (2^8): any common reference
+// cancels in y / z, so skipping the rescale is exact while every probability
+// stays <= 256.  A rescale is therefore rare after the first tiles.
+#include "internal.h"
+
+namespace ringattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) unsigned char lds_t;
+
+constexpr float kLazy = 8.0f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int D>
+struct Step {
+  static constexpr int TILE = kKeyTile * D * 2;  // bytes of one key (or value) tile
+  static constexpr int DT = D / 32;              // 32-row subtiles of O^T
+  static constexpr int KS = D / 16;              // k-steps of the score contraction
+  static constexpr int CHUNKS = TILE / 1024;     // 1 KB direct-load chunks per tile
+  static constexpr int PER_WAVE = CHUNKS / kStepWaves;
+
+  // Direct global -> LDS copy of one tile; each wave moves PER_WAVE chunks of
+  // 1 KB (64 lanes x 16 bytes), landing verbatim at the same offset in LDS.
+  static __device__ __forceinline__ void load_tile(const unsigned char* g, lds_t* l, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int c = wave * PER_WAVE + i;
+      __builtin_amdgcn_global_load_lds(g + c * 1024 + lane * 16, l + c * 1024, 16, 0, 0);
+    }
+  }
+
+  // S^T of one half tile (32 keys, rows half*32 ..) x 64 queries: s[nt].
+  static __device__ __forceinline__ void scores(f32x16 (&s)[2], const lds_t* kb, int half, const bf16x8 (&qf)[2][KS],
+                                                int l32, int hi) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
+    const int row = half * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
+          kb + key_tile_off(D, row, ks * 2 + hi));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) s[nt] = mfma(kf, qf[nt][ks], s[nt]);
+    }
+  }
+
+  // Key index (within the tile) held by accumulator register r of a half tile.
+  static __device__ __forceinline__ int key_of(int half, int r, int hi) {
+    return half * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+  }
+
+  // Row maxima (raw units) of a half tile for both 32-query tiles.
+  static __device__ __forceinline__ void rowmax(const f32x16 (&s)[2], float (&mx)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float m = fmaxf(fmaxf(s[nt][0], s[nt][1]), s[nt][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[nt][r]), s[nt][r + 1]);
+      m = fmaxf(m, s[nt][15]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      mx[nt] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+  }
+
+  // Raise the running reference where a maximum exceeds it by more than kLazy;
+  // rescale y and z by exp2(m_old - m_new) when any lane of the wave did.
+  static __device__ __forceinline__ void decide(const float (&mx)[2], float (&mref)[2], float (&zs)[2],
+                                                f32x16 (&o)[2][DT], float sl2) {
+    float alpha[2];
+    bool any = false;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float mt = mx[nt] * sl2;
+      const bool need = mt > mref[nt] + kLazy;
+      alpha[nt] = need ? exp2_fast(mref[nt] - mt) : 1.0f;
+      mref[nt] = need ? mt : mref[nt];
+      any |= need;
+    }
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        zs[nt] *= alpha[nt];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[nt][dt][r] *= alpha[nt];
+      }
+    }
+  }
+
+  // Probabilities of a half tile packed to bf16 in the order the PV MFMA
+  // consumes them: pb[nt][gg] = registers gg*8 .. gg*8+7 (16 keys); z
+  // accumulates the unrounded fp32 values.
+  static __device__ __forceinline__ void probs(const f32x16 (&s)[2], const float (&mref)[2], float (&zs)[2],
+                                               bf16x8 (&pb)[2][2], float sl2) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float mu = (mref[nt] == -INFINITY) ? 0.f : mref[nt];
+      float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = exp2_fast(fmaf(s[nt][gg * 8 + e], sl2, -mu));
+          const float p1 = exp2_fast(fmaf(s[nt][gg * 8 + e + 1], sl2, -mu));
+          z0 += p0;
+          z1 += p1;
+          const f32x2 pp = {p0, p1};
+          const bf16x2 pk = __builtin_convertvector(pp, bf16x2);
+          pb[nt][gg][e] = pk[0];
+          pb[nt][gg][e + 1] = pk[1];
+        }
+      }
+      zs[nt] += z0 + z1;
+    }
+  }
+
+  // O^T += V^T P^T for the 32 keys of one half tile (key groups 2*half, 2*half+1).
+  static __device__ __forceinline__ void pv(f32x16 (&o)[2][DT], const lds_t* vb, int half, const bf16x8 (&pb)[2][2],
+                                            int l32, int hi) {
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const int g = half * 2 + gg;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int row = dt * 32 + l32;
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
+            vb + val_tile_off(row, g * 2 + hi));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) o[nt][dt] = mfma(vf, pb[nt][gg], o[nt][dt]);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_all_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void step_bf16_kernel(StepBf16Args a) {
+  using S = Step<D>;
+  constexpr int DT = S::DT;
+  constexpr int KS = S::KS;
+  // Three key buffers (tile t in t % 3) and two value buffers (t % 2): key
+  // tile t+2 streams in while tiles t and t+1 are read.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[5 * S::TILE];
+  lds_t* smem = (lds_t*)(smem_raw);
+  auto kbuf = [smem](int t) { return smem + (t % 3) * S::TILE; };
+  auto vbuf = [smem](int t) { return smem + (3 + (t & 1)) * S::TILE; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // Heaviest work first: under a causal mask the last query rows see the most keys.
+  const int kvh = blockIdx.x % a.Hkv;
+  const int wgi = a.wgs_per_head - 1 - (int)(blockIdx.x / a.Hkv);
+  const int item = wgi * kStepWaves + wave;
+  const bool active = item < a.items;
+  const int it = active ? item : a.items - 1;
+  const int pblk = it / a.G;
+  const int hq = kvh * a.G + it % a.G;
+  const int q0 = pblk * kWaveRows;
+
+  // Tile counts.  Items are ordered row block first, so the first item of the
+  // workgroup has the lowest rows (fewest keys) and the last the highest.
+  auto keys_upto = [&](int qe) { return a.shift < 0 ? a.b : max(0, min(a.b, qe - a.shift)); };
+  auto full_upto = [&](int qlo) { return a.shift < 0 ? a.b : max(0, min(a.b, qlo + 1 - a.shift)); };
+  const int first_item = wgi * kStepWaves;
+  const int last_item = min(first_item + kStepWaves - 1, a.items - 1);
+  const int T = (keys_upto(min((last_item / a.G) * kWaveRows + kWaveRows, a.b)) + kKeyTile - 1) / kKeyTile;
+  const int F = min(T, full_upto((first_item / a.G) * kWaveRows) / kKeyTile);  // pipelined tiles
+  const int my_tiles = active ? (keys_upto(min(q0 + kWaveRows, a.b)) + kKeyTile - 1) / kKeyTile : 0;
+  const int my_full = full_upto(q0) / kKeyTile;
+
+  // Query fragments: B operand of S^T, lane holds query q0 + nt*32 + l32,
+  // d = ks*16 + hi*8 .. +7.  Rows past b are clamped (computed, never stored).
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int qi = min(q0 + nt * 32 + l32, a.b - 1);
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(a.q + ((size_t)qi * a.Hq + hq) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[nt][ks] = src[ks * 2 + hi];
+  }
+
+  // Running state.
+  f32x16 o[2][DT];
+  float mref[2], zs[2];
+  const size_t ig = (size_t)hq * a.npb + pblk;
+  float* cy = a.cy + ig * (size_t)(2 * DT * 16 * 64);
+  float* cm = a.cm + ig * 128;
+  float* cz = a.cz + ig * 128;
+  if (a.carry_in && active) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      mref[nt] = cm[nt * 64 + lane];
+      zs[nt] = cz[nt * 64 + lane];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[nt][dt][r] = cy[((nt * DT + dt) * 16 + r) * 64 + lane];
+    }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      mref[nt] = -INFINITY;
+      zs[nt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[nt][dt][r] = 0.f;
+    }
+  }
+
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.kp) + (size_t)kvh * a.npb * S::TILE;
+  const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.vp) + (size_t)kvh * a.npb * S::TILE;
+  auto issue_k = [&](int t) { S::load_tile(kg + (size_t)t * S::TILE, kbuf(t), wave, lane); };
+  auto issue_v = [&](int t) { S::load_tile(vg + (size_t)t * S::TILE, vbuf(t), wave, lane); };
+
+  // Every iteration t (pipelined or not) issues K(t+2) and V(t+1); the
+  // prologue issues K(0), V(0), K(1).  At the top of iteration t, K(t), V(t)
+  // and (when it exists) K(t+1) are resident.
+  if (T > 0) {
+    issue_k(0);
+    issue_v(0);
+  }
+  if (T > 1) issue_k(1);
+  wait_all_and_sync();
+
+  f32x16 sa[2], sb[2];
+  float mxa[2], mxb[2];
+  bf16x8 pb[2][2];
+  if (F >= 1) {
+    S::scores(sa, kbuf(0), 0, qf, l32, hi);
+    S::rowmax(sa, mxa);
+  }
+
+  // Pipelined full tiles.  Half A: scores of half 1 while the probabilities of
+  // half 0 feed PV; half B: scores of the next tile's half 0 while half 1 does.
+  int t = 0;
+  for (; t + 1 < F; ++t) {
+    if (t + 2 < T) issue_k(t + 2);
+    issue_v(t + 1);
+    S::decide(mxa, mref, zs, o, a.sl2);
+    S::scores(sb, kbuf(t), 1, qf, l32, hi);
+    S::probs(sa, mref, zs, pb, a.sl2);
+    S::pv(o, vbuf(t), 0, pb, l32, hi);
+    S::rowmax(sb, mxb);
+    S::decide(mxb, mref, zs, o, a.sl2);
+    S::scores(sa, kbuf(t + 1), 0, qf, l32, hi);
+    S::probs(sb, mref, zs, pb, a.sl2);
+    S::pv(o, vbuf(t), 1, pb, l32, hi);
+    S::rowmax(sa, mxa);
+    wait_all_and_sync();
+  }
+  if (t < F) {  // last full tile: no next scores
+    if (t + 2 < T) issue_k(t + 2);
+    if (t + 1 < T) issue_v(t + 1);
+    S::decide(mxa, mref, zs, o, a.sl2);
+    S::scores(sb, kbuf(t), 1, qf, l32, hi);
+    S::probs(sa, mref, zs, pb, a.sl2);
+    S::pv(o, vbuf(t), 0, pb, l32, hi);
+    S::rowmax(sb, mxb);
+    S::decide(mxb, mref, zs, o, a.sl2);
+    S::probs(sb, mref, zs, pb, a.sl2);
+    S::pv(o, vbuf(t), 1, pb, l32, hi);
+    wait_all_and_sync();
+    ++t;
+  }
+
+  // Remaining tiles: element masks (causal diagonal, ragged tail) and waves
+  // whose rows end earlier than the workgroup's.
+  for (; t < T; ++t) {
+    if (t + 2 < T) issue_k(t + 2);
+    if (t + 1 < T) issue_v(t + 1);
+    if (t < my_tiles) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        S::scores(sa, kbuf(t), half, qf, l32, hi);
+        if (t >= my_full) {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const int qi = q0 + nt * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = t * kKeyTile + S::key_of(half, r, hi);
+              const bool ok = key < a.b && (a.shift < 0 || key <= qi - a.shift);
+              if (!ok) sa[nt][r] = -INFINITY;
+            }
+          }
+        }
+        S::rowmax(sa, mxa);
+        S::decide(mxa, mref, zs, o, a.sl2);
+        S::probs(sa, mref, zs, pb, a.sl2);
+        S::pv(o, vbuf(t), half, pb, l32, hi);
+      }
+    }
+    wait_all_and_sync();
+  }
+
+  if (!active) return;
+
+  if (a.last) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float zt = zs[nt] + __shfl_xor(zs[nt], 32);
+      const int qi = q0 + nt * 32 + l32;
+      if (qi < a.b) {
+        const float inv = zt > 0.f ? 1.0f / zt : 0.f;
+        __bf16* orow = a.out + ((size_t)qi * a.Hq + hq) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const f32x2 lo = {o[nt][dt][rg * 4 + 0] * inv, o[nt][dt][rg * 4 + 1] * inv};
+            const f32x2 hv = {o[nt][dt][rg * 4 + 2] * inv, o[nt][dt][rg * 4 + 3] * inv};
+            uint2 w;
+            w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+            w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hv, bf16x2));
+            *reinterpret_cast<uint2*>(orow + dt * 32 + rg * 8 + hi * 4) = w;
+          }
+        if (a.lse && hi == 0)
+          a.lse[(size_t)hq * a.b + qi] = zt > 0.f ? (mref[nt] + __log2f(zt)) * kLn2 : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      cm[nt * 64 + lane] = mref[nt];
+      cz[nt * 64 + lane] = zs[nt];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cy[((nt * DT + dt) * 16 + r) * 64 + lane] = o[nt][dt][r];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st) {
+  const unsigned grid = (unsigned)a.wgs_per_head * (unsigned)a.Hkv;
+  if (D == 128)
+    hipLaunchKernelGGL(step_bf16_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(step_bf16_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ringattn

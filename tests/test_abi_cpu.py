@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects bad arguments before making any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ring_attention_block_step_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ringattn.h")
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on these paths
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _lib():
+    if not os.path.exists(ra.LIB_PATH):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return ra.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(ringattn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared() == sorted(ra.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ra.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(ringattn_[a-z0-9_]+)\b", out))
+    assert set(_declared()) <= exported
+
+
+def test_version_and_status_strings():
+    L = _lib()
+    assert b"gfx950" in L.ringattn_version()
+    assert L.ringattn_status_string(0) == b"ok"
+    assert L.ringattn_status_string(1) == b"invalid argument"
+    assert L.ringattn_status_string(2) == b"unsupported"
+    assert L.ringattn_status_string(3) == b"HIP runtime error"
+
+
+def _fwd(fn, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, N=1024, P=4, rank=0, Hq=4, Hkv=2, d=128,
+                causal=1, layout=0, stream=None)
+    args.update(kw)
+    return fn(args["q"], args["k"], args["v"], args["out"], args["lse"], args["N"], args["P"], args["rank"],
+              args["Hq"], args["Hkv"], args["d"], args["causal"], args["layout"], args["stream"])
+
+
+@pytest.mark.parametrize("entry", ["ringattn_forward", "ringattn_forward_f32"])
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "non-null"),
+    (dict(out=None), 1, "non-null"),
+    (dict(k=MISALIGNED), 1, "aligned"),
+    (dict(lse=MISALIGNED), 1, "aligned"),
+    (dict(P=0), 1, "P must be"),
+    (dict(N=3, P=4), 1, "N must be >= P"),
+    (dict(N=1023), 1, "multiple of P"),
+    (dict(rank=4), 1, "rank"),
+    (dict(rank=-1), 1, "rank"),
+    (dict(Hq=3, Hkv=2), 1, "Hq"),
+    (dict(Hkv=0), 1, "Hq"),
+    (dict(causal=2), 1, "causal"),
+    (dict(layout=2), 1, "layout"),
+    (dict(d=96), 2, "d_h"),
+    (dict(d=256), 2, "d_h"),
+])
+def test_forward_rejects_bad_arguments(entry, kw, status, needle):
+    L = _lib()
+    rc = _fwd(getattr(L, entry), **kw)
+    assert rc == status
+    assert needle in L.ringattn_last_error().decode()
+
+
+def test_merge_rejects_bad_arguments_and_accepts_empty():
+    L = _lib()
+    m = L.ringattn_merge
+    assert m(None, FAKE, FAKE, 2, 10, 4, 128, FAKE, 0, None, None) == 1
+    assert m(FAKE, FAKE, FAKE, 0, 10, 4, 128, FAKE, 0, None, None) == 1
+    assert m(FAKE, FAKE, FAKE, 2, -1, 4, 128, FAKE, 0, None, None) == 1
+    assert m(FAKE, FAKE, FAKE, 2, 10, 0, 128, FAKE, 0, None, None) == 1
+    assert m(FAKE, FAKE, FAKE, 2, 10, 4, 128, FAKE, 2, None, None) == 1
+    assert m(FAKE, FAKE, MISALIGNED, 2, 10, 4, 128, FAKE, 0, None, None) == 1
+    assert m(FAKE, FAKE, FAKE, 2, 10, 4, 32, FAKE, 0, None, None) == 2
+    # zero rows: valid, nothing to do, no HIP call
+    assert m(FAKE, FAKE, FAKE, 2, 0, 4, 128, FAKE, 0, None, None) == 0
+
+
+def test_timing_collect_empty():
+    _lib()
+    ra.timing_enable(False)
+    assert ra.timing_collect() == {"step_ms": 0.0, "step_launches": 0, "merge_ms": 0.0, "merge_launches": 0}
+
+
+def test_binding_raises_on_error_status():
+    L = _lib()
+    rc = _fwd(L.ringattn_forward, P=0)
+    with pytest.raises(ra.RingAttnError) as ei:
+        ra._check(rc)
+    assert ei.value.status == 1
+
+
+def test_shard_helpers_match_layout_definitions():
+    import torch
+    N, P = 24, 4
+    b = N // P
+    for r in range(P):
+        assert ra.shard_index(N, P, "contiguous", r).tolist() == list(range(r * b, r * b + b))
+        assert ra.shard_index(N, P, "striped", r).tolist() == [j * P + r for j in range(b)]
+    x = torch.arange(N * 3).view(N, 3)
+    for layout in ("contiguous", "striped"):
+        packed = ra.pack_shards(x, P, layout)
+        for r in range(P):
+            assert torch.equal(packed[r], x[ra.shard_index(N, P, layout, r)])

@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small shapes compare every row; they span several 64-key tiles, several
+64-row query blocks and a ragged tail (b not a multiple of 64).  The named
+full-size workloads compare a seeded sample of rows at their real shapes, in
+the launch configuration the bench times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_attention_block_step_amd as ra
+import workloads as wl
+from parity_util import TOL, check, compare, gpu_inputs, oracle_rows, run_and_compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(name, **kw):
+    base = dict(N=1024, P=4, ranks=(0,), layout="contiguous", causal=True, Hq=4, Hkv=2, d=128,
+                dtype="bf16", seed=11)
+    base.update(kw)
+    return wl.Workload(name, **base)
+
+
+SMALL = [
+    # ragged b = 200 (3 tiles + 8), GQA 4/2, both layouts, every rank
+    _w("ragged-contig-causal", N=800, P=4, ranks=(0, 1, 2, 3)),
+    _w("ragged-striped-causal", N=800, P=4, ranks=(0, 1, 2, 3), layout="striped"),
+    _w("contig-noncausal", N=1024, P=4, ranks=(0, 3), causal=False),
+    _w("striped-noncausal-d64", N=1024, P=4, ranks=(2,), causal=False, layout="striped", d=64),
+    _w("contig-causal-d64-mha", N=1536, P=2, ranks=(0, 1), Hq=2, Hkv=2, d=64),
+    _w("gqa8-striped", N=2048, P=8, ranks=(0, 5, 7), Hq=8, Hkv=1, layout="striped"),
+    _w("gqa3-contig", N=960, P=3, ranks=(2,), Hq=6, Hkv=2),
+    _w("p1-causal", N=333, P=1, ranks=(0,), Hq=4, Hkv=4),
+    _w("p1-noncausal-tiny", N=5, P=1, ranks=(0,), causal=False, Hq=1, Hkv=1),
+    _w("b1-striped", N=8, P=8, ranks=(0, 3, 7), layout="striped", Hq=2, Hkv=1),
+    _w("kscale-wide-spread", N=1024, P=4, ranks=(3,), k_scale=4.0),
+    _w("uniform-v", N=768, P=4, ranks=(3,), v_dist="uniform", Hq=8, Hkv=2),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_bf16_small_all_rows(w):
+    k_glob, v_glob = wl.global_kv(w)
+    for rank in w.ranks:
+        stats = run_and_compare(w, rank, None, k_glob=k_glob, v_glob=v_glob)
+        check(w, stats)
+
+
+F32_SMALL = [
+    wl.WORKLOADS["tiny-ring-f32"],
+    _w("f32-ragged-causal-gqa", N=600, P=4, ranks=(0, 3), Hq=4, Hkv=2, d=128, dtype="f32"),
+    _w("f32-striped-causal", N=512, P=8, ranks=(0, 6), Hq=2, Hkv=1, d=64, dtype="f32", layout="striped"),
+]
+
+
+@pytest.mark.parametrize("w", F32_SMALL, ids=[w.name for w in F32_SMALL])
+def test_f32_all_rows(w):
+    k_glob, v_glob = wl.global_kv(w)
+    for rank in w.ranks:
+        stats = run_and_compare(w, rank, None, k_glob=k_glob, v_glob=v_glob)
+        check(w, stats)
+
+
+def test_tiny_ring_f32_all_ranks_equal_dense():
+    """The tiny fp32 workload: all 4 ranks' outputs, concatenated in global order,
+    against dense softmax attention over the whole sequence."""
+    w = wl.WORKLOADS["tiny-ring-f32"]
+    k_glob, v_glob = wl.global_kv(w)
+    outs = []
+    for rank in range(w.P):
+        q, k, v = gpu_inputs(w, rank, k_glob, v_glob)
+        out, _ = ra.forward(q, k, v, P=w.P, rank=rank, causal=w.causal, layout=w.layout)
+        outs.append(out.cpu().double().numpy())
+    got = np.concatenate(outs)
+    q_all = wl.query_rows(w, np.arange(w.N)).double().numpy()
+    want, _ = oracle.dense_attention(q_all, np.arange(w.N), k_glob.double().numpy(), v_glob.double().numpy(),
+                                     w.causal)
+    assert np.abs(got - want).max() <= TOL["f32"]["max_abs"]
+
+
+FULL = [
+    ("32k-contiguous-causal", 256),
+    ("32k-striped-causal", 256),
+    ("128k-contiguous-causal", 64),
+    ("1m-contiguous-causal", 64),
+]
+
+
+@pytest.mark.parametrize("name,rows", FULL, ids=[n for n, _ in FULL])
+def test_bf16_full_size_sampled_rows(name, rows):
+    w = wl.WORKLOADS[name]
+    stats = run_and_compare(w, w.ranks[0], rows)
+    check(w, stats)
+
+
+@pytest.mark.parametrize("name", ["32k-contiguous-causal", "32k-striped-causal"])
+def test_bf16_32k_every_row_of_two_heads(name):
+    """Every query row of the first and the last query head (key/value heads 0
+    and 7), at the full 32k shape."""
+    w = wl.WORKLOADS[name]
+    rank = w.ranks[0]
+    k_glob, v_glob = wl.global_kv(w)
+    q, k, v = gpu_inputs(w, rank, k_glob, v_glob)
+    out, lse = ra.forward(q, k, v, P=w.P, rank=rank, causal=w.causal, layout=w.layout)
+    torch.cuda.synchronize()
+    heads = [0, w.Hq - 1]
+    kvh = [h // (w.Hq // w.Hkv) for h in heads]
+    tq = oracle.shard_positions(w.layout, rank, w.P, w.b)
+    q_or = wl.query_rows(w, tq)[:, heads, :].double().numpy()
+    want_o, want_lse = oracle.dense_attention(q_or, tq, k_glob[:, kvh, :].double().numpy(),
+                                              v_glob[:, kvh, :].double().numpy(), w.causal)
+    stats = compare(w, out.float().cpu().numpy()[:, heads, :], lse.cpu().numpy()[heads], want_o, want_lse)
+    print(f"[gpu]   -> {stats}", flush=True)
+    check(w, stats)
+
+
+def test_equal_keys_give_mean_of_allowed_values():
+    """All keys equal: O is the mean of the allowed values (prefix mean under the
+    causal mask); LSE = S0 + ln(count)."""
+    N, P, Hq, Hkv, d = 640, 4, 2, 1, 128
+    b = N // P
+    key = torch.randn(d, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    k_glob = key.expand(N, Hkv, d).contiguous()
+    v_glob = (torch.rand(N, Hkv, d, generator=torch.Generator().manual_seed(2)) * 2 - 1).to(torch.bfloat16)
+    q_glob = torch.randn(N, Hq, d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    vv = v_glob.double().numpy()[:, 0, :]
+    prefix = np.cumsum(vv, axis=0) / np.arange(1, N + 1)[:, None]
+    for layout in ("contiguous", "striped"):
+        for rank in (0, 3):
+            idx = ra.shard_index(N, P, layout, rank)
+            q = q_glob[idx].cuda()
+            out, lse = ra.forward(q, ra.pack_shards(k_glob, P, layout).cuda(),
+                                  ra.pack_shards(v_glob, P, layout).cuda(), P=P, rank=rank, causal=True,
+                                  layout=layout)
+            tq = oracle.shard_positions(layout, rank, P, b)
+            got = out.cpu().double().numpy()
+            for h in range(Hq):
+                assert np.abs(got[:, h, :] - prefix[tq]).max() <= 1e-2
+                s0 = q_glob[tq, h].double().numpy() @ key.double().numpy() / np.sqrt(d)
+                assert np.abs(lse.cpu().numpy()[h] - (s0 + np.log(tq + 1))).max() <= 1e-3
+
+
+def test_serial_and_overlapped_hops_are_bit_identical():
+    """The double buffer on the second stream must not race: outputs with the hop
+    copies serialised on the caller stream are bit-identical."""
+    w = _w("race", N=8192, P=8, ranks=(7,), Hq=8, Hkv=2)
+    q, k, v = gpu_inputs(w, 7)
+    outs = []
+    try:
+        for serial in (False, True, False):
+            ra.set_serial_hops(serial)
+            out, lse = ra.forward(q, k, v, P=w.P, rank=7, causal=True, layout="contiguous")
+            torch.cuda.synchronize()
+            outs.append((out.clone(), lse.clone()))
+    finally:
+        ra.set_serial_hops(False)
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_forward_on_side_stream_and_deterministic():
+    w = _w("stream", N=4096, P=4, ranks=(2,), Hq=8, Hkv=2, layout="striped")
+    q, k, v = gpu_inputs(w, 2)
+    ref, ref_lse = ra.forward(q, k, v, P=w.P, rank=2, causal=True, layout=w.layout)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out, lse = ra.forward(q, k, v, P=w.P, rank=2, causal=True, layout=w.layout)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n,rows,Hq,d", [(8, 300, 4, 128), (3, 77, 2, 64), (1, 5, 1, 128)])
+def test_merge_matches_oracle(out_dtype, n, rows, Hq, d):
+    g = torch.Generator().manual_seed(n * 1000 + rows)
+    m = torch.randn(n, Hq, rows, generator=g) * 4
+    z = torch.rand(n, Hq, rows, generator=g) * 3 + 0.1
+    y = torch.randn(n, rows, Hq, d, generator=g)
+    if n > 1:   # some empty partials (-inf, 0, 0)
+        empty = torch.rand(n, Hq, rows, generator=g) < 0.2
+        m[empty] = -float("inf")
+        z[empty] = 0.0
+        y.permute(0, 2, 1, 3)[empty] = 0.0
+    if rows > 2:   # one row with every partial empty
+        m[:, 0, 2] = -float("inf")
+        z[:, 0, 2] = 0.0
+        y[:, 2, 0, :] = 0.0
+    out, lse = ra.merge(m.cuda(), z.cuda(), y.cuda(), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    want_o, want_lse = oracle.merge_partials(m.double().numpy().transpose(0, 2, 1),
+                                             z.double().numpy().transpose(0, 2, 1), y.double().numpy())
+    got = out.cpu().double().numpy()
+    # fp32: relative to the output scale; bf16: plus the final rounding (2^-9 relative)
+    scale = np.abs(want_o).max() + 1e-30
+    tol = 2e-6 * scale if out_dtype == torch.float32 else 2 ** -8 * scale
+    assert np.abs(got - want_o).max() <= tol
+    got_lse = lse.cpu().double().numpy().T
+    fin = np.isfinite(want_lse)
+    assert np.array_equal(np.isfinite(got_lse), fin)
+    assert np.abs(got_lse[fin] - want_lse[fin]).max() <= 1e-5 * (1 + np.abs(want_lse[fin]).max())
+
+
+def test_merge_of_gpu_block_partials_equals_forward():
+    """Per-block partial triples of the oracle's fold, merged on the GPU, equal the
+    oracle's dense result (the merge is the decode-style combine of the pages)."""
+    rng = np.random.default_rng(4)
+    P, b, Hq, Hkv, d = 4, 96, 2, 1, 64
+    N = P * b
+    q = rng.standard_normal((N, Hq, d))
+    k = rng.standard_normal((N, Hkv, d))
+    v = rng.standard_normal((N, Hkv, d))
+    u = 2
+    tq = oracle.shard_positions("contiguous", u, P, b)
+    ms, zs, ys = [], [], []
+    for r in range(P):
+        tk = oracle.shard_positions("contiguous", r, P, b)
+        allow = oracle.allowed_mask(tq, tk, True)
+        m, z, y = oracle.empty_state(b, Hq, d)
+        for h in range(Hq):
+            s = np.where(allow, q[tq, h] @ k[tk, 0].T / np.sqrt(d), -np.inf)
+            m[h], z[h], y[:, h, :] = oracle.online_fold(m[h], z[h], y[:, h, :], s, v[tk, 0])
+        ms.append(m)
+        zs.append(z)
+        ys.append(y)
+    mt = torch.tensor(np.stack(ms), dtype=torch.float32).cuda()
+    zt = torch.tensor(np.stack(zs), dtype=torch.float32).cuda()
+    yt = torch.tensor(np.stack(ys), dtype=torch.float32).cuda()
+    out, lse = ra.merge(mt, zt, yt, out_dtype=torch.float32)
+    want_o, want_lse = oracle.dense_attention(q[tq], tq, k, v, True)
+    assert np.abs(out.cpu().double().numpy() - want_o).max() <= 1e-5
+    assert np.abs(lse.cpu().double().numpy() - want_lse).max() <= 1e-5
+
+
+def test_timing_counts_step_launches():
+    w = _w("timing", N=2048, P=8, ranks=(7,))
+    q, k, v = gpu_inputs(w, 7)
+    ra.timing_collect()
+    ra.timing_enable(True)
+    try:
+        ra.forward(q, k, v, P=8, rank=7, causal=True, layout="contiguous")
+        ra.forward(q, k, v, P=8, rank=3, causal=True, layout="contiguous")   # blocks 4..7 skipped
+        t = ra.timing_collect()
+    finally:
+        ra.timing_enable(False)
+    assert t["step_launches"] == 8 + 4
+    assert t["step_ms"] > 0
