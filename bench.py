@@ -149,6 +149,64 @@ def cpu_baseline(w, rank, k_glob, v_glob, seconds: float, gpu_out=None, gpu_lse=
 
 
 # ---------------------------------------------------------------------------
+# The triple-merge kernel (HBM-bound) and a plain copy for counter calibration.
+# ---------------------------------------------------------------------------
+
+MERGE_SHAPE = {"nparts": 8, "rows": 16384, "Hq": 32, "d_h": 128}
+
+
+def merge_bytes(nparts: int, rows: int, Hq: int, d: int, out_bytes: int = 2) -> int:
+    """Algorithmic HBM bytes of one merge: every (m, z, y) read once, O and LSE
+    written once."""
+    return nparts * rows * Hq * (4 * d + 8) + rows * Hq * (out_bytes * d + 4)
+
+
+def measure_merge(reps: int = 10) -> dict:
+    """Time ringattn_merge on seeded partial triples (HIP events around each
+    kernel, inside the library) and report achieved GB/s against 8 TB/s."""
+    import torch
+
+    import ring_attention_block_step_amd as ra
+
+    n, rows, Hq, d = (MERGE_SHAPE[k] for k in ("nparts", "rows", "Hq", "d_h"))
+    g = torch.Generator(device="cuda").manual_seed(7)
+    m = torch.randn(n, Hq, rows, device="cuda", generator=g) * 4
+    z = torch.rand(n, Hq, rows, device="cuda", generator=g) + 0.5
+    y = torch.randn(n, rows, Hq, d, device="cuda", generator=g)
+    out = torch.empty(rows, Hq, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(Hq, rows, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        ra.merge(m, z, y, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ra.timing_collect()
+    ra.timing_enable(True)
+    for _ in range(reps):
+        ra.merge(m, z, y, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ra.timing_enable(False)
+    t = ra.timing_collect()
+    avg_ms = t["merge_ms"] / max(1, t["merge_launches"])
+    nbytes = merge_bytes(n, rows, Hq, d)
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    return {"kernel": "merge_kernel<128,bf16>", "shape": dict(MERGE_SHAPE), "bytes_per_launch": nbytes,
+            "avg_launch_ms": avg_ms, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "launches": t["merge_launches"]}
+
+
+def copy_calibration(nbytes: int, reps: int = 3) -> None:
+    """A plain device copy of known size (torch's copy kernel), for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of other kernels."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+# ---------------------------------------------------------------------------
 # Main.
 # ---------------------------------------------------------------------------
 
@@ -160,6 +218,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="1m-contiguous-causal")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge", action="store_true", help="skip the merge-kernel measurement")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -177,6 +238,9 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         return 3
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return 0
     w = wl.WORKLOADS[args.workload]
     rank = w.ranks[-1]
     dev = torch.device("cuda:0")
@@ -238,6 +302,8 @@ def main(argv=None) -> int:
         "flops_per_launch": flops_per_launch,
     }
 
+    merge = None if args.no_merge else measure_merge()
+
     cpu, parity = None, None
     if not args.no_cpu_baseline:
         gpu_out = out.float().cpu().numpy()
@@ -262,6 +328,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity_sample": parity,
+        "merge_kernel": merge,
     }
     print(json.dumps(line), flush=True)
     return 0
