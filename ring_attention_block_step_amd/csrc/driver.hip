@@ -26,7 +26,7 @@
 #include <cstdio>
 #include <cstdarg>
 
-#include "../../include/ringattn.h"
+#include "ringattn.h"
 #include "internal.h"
 
 using namespace ringattn;

@@ -7,10 +7,15 @@
 
 namespace ringattn {
 
-// Key tile of the bf16 step kernel, and the query rows one wavefront owns.
+// Key tile of the bf16 step kernel; query rows one wavefront owns (kStepNT
+// tiles of 32) and wavefronts per workgroup (256 query rows per workgroup).
+#ifndef RINGATTN_STEP_NT
+#define RINGATTN_STEP_NT 1
+#endif
 constexpr int kKeyTile = 64;
-constexpr int kWaveRows = 64;
-constexpr int kStepWaves = 4;
+constexpr int kStepNT = RINGATTN_STEP_NT;
+constexpr int kWaveRows = 32 * kStepNT;
+constexpr int kStepWaves = 8 / kStepNT;
 
 // Mask of one visiting block, in LOCAL row indices (query row i, key row j):
 //   kMaskNone   every key row j < b is allowed;
@@ -23,11 +28,11 @@ constexpr int kMaskNone = -1;
 
 struct StepBf16Args {
   const __bf16* q;   // [b, Hq, D] caller's query rows
-  const __bf16* kp;  // slot keys   [Hkv][bpad/64] tiles of 64 x D, swizzled (key_tile_off)
-  const __bf16* vp;  // slot values [Hkv][bpad/64] tiles of D x 64, transposed, swizzled (val_tile_off)
-  float* cy;         // running y   [Hq*npb][2][D/32][16][64]  (register order)
-  float* cm;         // running m   [Hq*npb][2][64]  (log2 units, scaled)
-  float* cz;         // running z   [Hq*npb][2][64]  (per-lane partial sums)
+  const __bf16* kp;  // slot keys   [Hkv][bpad/64] tiles of 64 x D, chunk-major (key_tile_off)
+  const __bf16* vp;  // slot values [Hkv][bpad/64] tiles of D x 64, transposed, chunk-major (val_tile_off)
+  float* cy;         // running y   [Hq*npb][kStepNT][D/32][16][64]  (register order)
+  float* cm;         // running m   [Hq*npb][kStepNT][64]  (log2 units, scaled)
+  float* cz;         // running z   [Hq*npb][kStepNT][64]  (per-lane partial sums)
   __bf16* out;       // [b, Hq, D]
   float* lse;        // [Hq, b] or null
   int b, bpad, npb, Hq, Hkv, G;
@@ -55,14 +60,16 @@ struct StepF32Args {
 
 // Byte offset of 16-byte chunk `chunk` of row `row` inside one 64-key tile of a
 // slot, which is also its LDS image (tiles are copied to LDS verbatim).
-//  key tile:   64 rows (keys) x D bf16; row = 2*D bytes.
-//  value tile: D rows (d) x 64 keys bf16 (keys permuted in groups of 16); row = 128 bytes.
-// Chunks are XOR-swizzled so that the 32 lanes of a wave reading one chunk
-// column of 32 consecutive rows (the MFMA A-operand read) hit distinct banks.
-__host__ __device__ inline int key_tile_off(int D, int row, int chunk) {
-  return D == 128 ? row * 256 + ((chunk ^ (row & 15)) << 4) : row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
-}
-__host__ __device__ inline int val_tile_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+//  key tile:   64 rows (keys) x D bf16, chunk c = d 8c .. 8c+7;
+//  value tile: D rows (d) x 64 keys bf16 (keys permuted in groups of 16),
+//              chunk c = storage positions 8c .. 8c+7.
+// Chunk-major: all rows' chunk c are contiguous.  The MFMA A-operand read (32
+// lanes, 32 consecutive rows, one chunk) is then 512 contiguous bytes, free of
+// bank conflicts, and a lane's successive chunks are a fixed stride apart, so
+// every fragment address is one base register plus an immediate.
+__host__ __device__ inline int key_tile_off(int row, int chunk) { return chunk * (64 * 16) + row * 16; }
+template <int D>
+__host__ __device__ inline int val_tile_off(int row, int chunk) { return chunk * (D * 16) + row * 16; }
 
 // Round b up to whole key tiles.
 inline int64_t padded_rows(int64_t b) { return (b + kKeyTile - 1) / kKeyTile * kKeyTile; }

@@ -8,9 +8,9 @@
 // Slot layout: per key/value head h, tiles of 64 keys (bpad = b rounded up to
 // 64, rows b .. bpad-1 zero), each tile 64*D bf16 and copied to LDS verbatim:
 //   key tile t     row j (key), 16-byte chunk c (d = 8c .. 8c+7)
-//                  at byte key_tile_off(D, j, c);
+//                  at byte key_tile_off(j, c);
 //   value tile t   transposed: row d, chunk c holding 8 keys, at byte
-//                  val_tile_off(d, c).  Inside each group of 16 keys the
+//                  val_tile_off<D>(d, c).  Inside each group of 16 keys the
 //                  storage order kappa holds key
 //                  perm(kappa) = (kappa & 3) | (kappa & 4) << 1 | (kappa & 8) >> 1,
 //                  the order in which the 32x32x16 MFMA accumulator of the
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* __restri
       vv = *reinterpret_cast<const uint4*>(v + src);
     }
     unsigned char* kt = reinterpret_cast<unsigned char*>(kp + ((size_t)h * ntiles + t) * (size_t)(D * T));
-    *reinterpret_cast<uint4*>(kt + key_tile_off(D, row, cc)) = kv;
+    *reinterpret_cast<uint4*>(kt + key_tile_off(row, cc)) = kv;
     uint16_t* dst = vs + row * VS + cc * 8;
     *reinterpret_cast<uint2*>(dst) = make_uint2(vv.x, vv.y);
     *reinterpret_cast<uint2*>(dst + 4) = make_uint2(vv.z, vv.w);
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* __restri
       }
       w[e / 2] = pair[0] | (pair[1] << 16);
     }
-    *reinterpret_cast<uint4*>(vt + val_tile_off(d, k0 / 8)) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(vt + val_tile_off<D>(d, k0 / 8)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 

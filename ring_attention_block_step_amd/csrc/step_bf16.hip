@@ -2,7 +2,7 @@
 // running (m, z, y) of every local query row ("Ring Attention" (aarnphm.xyz),
 // the recurrence for S, m, z, y; O = y / z after the last visit).
 //
-// Formulation.  Each wavefront owns 64 query rows of one query head and keeps
+// Formulation.  Each wavefront owns 32*NT query rows of one query head and keeps
 // everything per query in the SAME lane across both contractions:
 //   S^T = K Q^T     A = key tile rows from LDS, B = the wave's query rows
 //                   (held in registers for the whole launch);
@@ -13,11 +13,12 @@
 // statistics of a query live in two lanes (l and l ^ 32) and the rescale of O
 // by exp(m_old - m_new) is a per-lane multiply.
 //
-// Workgroup: 4 waves (one per SIMD) = 4 query items (query head, 64 rows) that
-// share one key/value head, so every key/value tile staged in LDS serves 256
-// queries.  Tiles of 64 keys move global -> LDS with direct-to-LDS loads
-// (global_load_lds_dwordx4), double-buffered; the slot layout already is the
-// swizzled LDS image.
+// Workgroup: 8/NT waves = 8/NT query items (query head, 32*NT rows) that share
+// one key/value head, so every key/value tile staged in LDS serves 256 queries
+// (NT = 2: one wave per SIMD; NT = 1: two waves per SIMD).  Tiles of 64 keys move global -> LDS with direct-to-LDS loads
+// (global_load_lds_dwordx4); the slot layout already is the LDS image, stored
+// chunk-major so the fragment reads are conflict-free and need no per-lane
+// address arithmetic.
 //
 // Software pipeline over the tiles every row of the workgroup sees in full:
 // iteration t issues the MFMAs of S(t+1) while the VALU computes the
@@ -50,13 +51,15 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D>
+template <int D, int NT>
 struct Step {
   static constexpr int TILE = kKeyTile * D * 2;  // bytes of one key (or value) tile
   static constexpr int DT = D / 32;              // 32-row subtiles of O^T
   static constexpr int KS = D / 16;              // k-steps of the score contraction
+  static constexpr int WAVES = 8 / NT;
   static constexpr int CHUNKS = TILE / 1024;     // 1 KB direct-load chunks per tile
-  static constexpr int PER_WAVE = CHUNKS / kStepWaves;
+  static constexpr int PER_WAVE = CHUNKS / WAVES;
+  static_assert(PER_WAVE >= 1 && CHUNKS % WAVES == 0, "tile chunks must split over the waves");
 
   // Direct global -> LDS copy of one tile; each wave moves PER_WAVE chunks of
   // 1 KB (64 lanes x 16 bytes), landing verbatim at the same offset in LDS.
@@ -68,20 +71,20 @@ struct Step {
     }
   }
 
-  // S^T of one half tile (32 keys, rows half*32 ..) x 64 queries: s[nt].
-  static __device__ __forceinline__ void scores(f32x16 (&s)[2], const lds_t* kb, int half, const bf16x8 (&qf)[2][KS],
+  // S^T of one half tile (32 keys, rows half*32 ..) x 32*NT queries: s[nt].
+  static __device__ __forceinline__ void scores(f32x16 (&s)[NT], const lds_t* kb, int half, const bf16x8 (&qf)[NT][KS],
                                                 int l32, int hi) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
     const int row = half * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
-          kb + key_tile_off(D, row, ks * 2 + hi));
+          kb + key_tile_off(row, ks * 2 + hi));
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) s[nt] = mfma(kf, qf[nt][ks], s[nt]);
+      for (int nt = 0; nt < NT; ++nt) s[nt] = mfma(kf, qf[nt][ks], s[nt]);
     }
   }
 
@@ -90,10 +93,10 @@ struct Step {
     return half * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
   }
 
-  // Row maxima (raw units) of a half tile for both 32-query tiles.
-  static __device__ __forceinline__ void rowmax(const f32x16 (&s)[2], float (&mx)[2]) {
+  // Row maxima (raw units) of a half tile for every 32-query tile.
+  static __device__ __forceinline__ void rowmax(const f32x16 (&s)[NT], float (&mx)[NT]) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       float m = fmaxf(fmaxf(s[nt][0], s[nt][1]), s[nt][2]);
 #pragma unroll
       for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[nt][r]), s[nt][r + 1]);
@@ -105,12 +108,12 @@ struct Step {
 
   // Raise the running reference where a maximum exceeds it by more than kLazy;
   // rescale y and z by exp2(m_old - m_new) when any lane of the wave did.
-  static __device__ __forceinline__ void decide(const float (&mx)[2], float (&mref)[2], float (&zs)[2],
-                                                f32x16 (&o)[2][DT], float sl2) {
-    float alpha[2];
+  static __device__ __forceinline__ void decide(const float (&mx)[NT], float (&mref)[NT], float (&zs)[NT],
+                                                f32x16 (&o)[NT][DT], float sl2) {
+    float alpha[NT];
     bool any = false;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const float mt = mx[nt] * sl2;
       const bool need = mt > mref[nt] + kLazy;
       alpha[nt] = need ? exp2_fast(mref[nt] - mt) : 1.0f;
@@ -119,7 +122,7 @@ struct Step {
     }
     if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         zs[nt] *= alpha[nt];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -132,10 +135,10 @@ struct Step {
   // Probabilities of a half tile packed to bf16 in the order the PV MFMA
   // consumes them: pb[nt][gg] = registers gg*8 .. gg*8+7 (16 keys); z
   // accumulates the unrounded fp32 values.
-  static __device__ __forceinline__ void probs(const f32x16 (&s)[2], const float (&mref)[2], float (&zs)[2],
-                                               bf16x8 (&pb)[2][2], float sl2) {
+  static __device__ __forceinline__ void probs(const f32x16 (&s)[NT], const float (&mref)[NT], float (&zs)[NT],
+                                               bf16x8 (&pb)[NT][2], float sl2) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const float mu = (mref[nt] == -INFINITY) ? 0.f : mref[nt];
       float z0 = 0.f, z1 = 0.f;
 #pragma unroll
@@ -157,7 +160,7 @@ struct Step {
   }
 
   // O^T += V^T P^T for the 32 keys of one half tile (key groups 2*half, 2*half+1).
-  static __device__ __forceinline__ void pv(f32x16 (&o)[2][DT], const lds_t* vb, int half, const bf16x8 (&pb)[2][2],
+  static __device__ __forceinline__ void pv(f32x16 (&o)[NT][DT], const lds_t* vb, int half, const bf16x8 (&pb)[NT][2],
                                             int l32, int hi) {
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
@@ -166,9 +169,9 @@ struct Step {
       for (int dt = 0; dt < DT; ++dt) {
         const int row = dt * 32 + l32;
         const bf16x8 vf = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
-            vb + val_tile_off(row, g * 2 + hi));
+            vb + val_tile_off<D>(row, g * 2 + hi));
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o[nt][dt] = mfma(vf, pb[nt][gg], o[nt][dt]);
+        for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma(vf, pb[nt][gg], o[nt][dt]);
       }
     }
   }
@@ -179,18 +182,37 @@ __device__ __forceinline__ void wait_all_and_sync() {
   __syncthreads();
 }
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// Wait until at most `n` vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at 7, lgkmcnt
+// 11:8 at 0), then a bare s_barrier.  __syncthreads() would add a workgroup
+// fence, which waits for every outstanding load (vmcnt 0); the loads left in
+// flight here only fill LDS buffers nobody reads before the next barrier.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+template <int n>
+__device__ __forceinline__ void wait_keep_and_sync() {
+  static_assert(n >= 0 && n < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(n | (7 << 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D, int NT>
+__global__ __attribute__((amdgpu_flat_work_group_size(512 / NT, 512 / NT), amdgpu_waves_per_eu(3 - NT, 3 - NT)))
 void step_bf16_kernel(StepBf16Args a) {
-  using S = Step<D>;
+  using S = Step<D, NT>;
+  constexpr int ROWS = 32 * NT;
+  constexpr int WAVES = S::WAVES;
   constexpr int DT = S::DT;
   constexpr int KS = S::KS;
-  // Three key buffers (tile t in t % 3) and two value buffers (t % 2): key
-  // tile t+2 streams in while tiles t and t+1 are read.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[5 * S::TILE];
+  // Four key buffers (tile t in t % 4) and three value buffers (t % 3):
+  // iteration t reads K(t), K(t+1), V(t) while V(t+2) and K(t+3) stream in, so
+  // every load has a whole iteration to land before it is waited for.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[7 * S::TILE];
   lds_t* smem = (lds_t*)(smem_raw);
-  auto kbuf = [smem](int t) { return smem + (t % 3) * S::TILE; };
-  auto vbuf = [smem](int t) { return smem + (3 + (t & 1)) * S::TILE; };
+  auto kbuf = [smem](int t) { return smem + (t & 3) * S::TILE; };
+  auto vbuf = [smem](int t) { return smem + (4 + t % 3) * S::TILE; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -201,29 +223,29 @@ void step_bf16_kernel(StepBf16Args a) {
   // Heaviest work first: under a causal mask the last query rows see the most keys.
   const int kvh = blockIdx.x % a.Hkv;
   const int wgi = a.wgs_per_head - 1 - (int)(blockIdx.x / a.Hkv);
-  const int item = wgi * kStepWaves + wave;
+  const int item = wgi * WAVES + wave;
   const bool active = item < a.items;
   const int it = active ? item : a.items - 1;
   const int pblk = it / a.G;
   const int hq = kvh * a.G + it % a.G;
-  const int q0 = pblk * kWaveRows;
+  const int q0 = pblk * ROWS;
 
   // Tile counts.  Items are ordered row block first, so the first item of the
   // workgroup has the lowest rows (fewest keys) and the last the highest.
   auto keys_upto = [&](int qe) { return a.shift < 0 ? a.b : max(0, min(a.b, qe - a.shift)); };
   auto full_upto = [&](int qlo) { return a.shift < 0 ? a.b : max(0, min(a.b, qlo + 1 - a.shift)); };
-  const int first_item = wgi * kStepWaves;
-  const int last_item = min(first_item + kStepWaves - 1, a.items - 1);
-  const int T = (keys_upto(min((last_item / a.G) * kWaveRows + kWaveRows, a.b)) + kKeyTile - 1) / kKeyTile;
-  const int F = min(T, full_upto((first_item / a.G) * kWaveRows) / kKeyTile);  // pipelined tiles
-  const int my_tiles = active ? (keys_upto(min(q0 + kWaveRows, a.b)) + kKeyTile - 1) / kKeyTile : 0;
+  const int first_item = wgi * WAVES;
+  const int last_item = min(first_item + WAVES - 1, a.items - 1);
+  const int T = (keys_upto(min((last_item / a.G) * ROWS + ROWS, a.b)) + kKeyTile - 1) / kKeyTile;
+  const int F = min(T, full_upto((first_item / a.G) * ROWS) / kKeyTile);  // pipelined tiles
+  const int my_tiles = active ? (keys_upto(min(q0 + ROWS, a.b)) + kKeyTile - 1) / kKeyTile : 0;
   const int my_full = full_upto(q0) / kKeyTile;
 
   // Query fragments: B operand of S^T, lane holds query q0 + nt*32 + l32,
   // d = ks*16 + hi*8 .. +7.  Rows past b are clamped (computed, never stored).
-  bf16x8 qf[2][KS];
+  bf16x8 qf[NT][KS];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const int qi = min(q0 + nt * 32 + l32, a.b - 1);
     const bf16x8* src = reinterpret_cast<const bf16x8*>(a.q + ((size_t)qi * a.Hq + hq) * D);
 #pragma unroll
@@ -231,15 +253,15 @@ void step_bf16_kernel(StepBf16Args a) {
   }
 
   // Running state.
-  f32x16 o[2][DT];
-  float mref[2], zs[2];
+  f32x16 o[NT][DT];
+  float mref[NT], zs[NT];
   const size_t ig = (size_t)hq * a.npb + pblk;
-  float* cy = a.cy + ig * (size_t)(2 * DT * 16 * 64);
-  float* cm = a.cm + ig * 128;
-  float* cz = a.cz + ig * 128;
+  float* cy = a.cy + ig * (size_t)(NT * DT * 16 * 64);
+  float* cm = a.cm + ig * (NT * 64);
+  float* cz = a.cz + ig * (NT * 64);
   if (a.carry_in && active) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       mref[nt] = cm[nt * 64 + lane];
       zs[nt] = cz[nt * 64 + lane];
 #pragma unroll
@@ -249,7 +271,7 @@ void step_bf16_kernel(StepBf16Args a) {
     }
   } else {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       mref[nt] = -INFINITY;
       zs[nt] = 0.f;
 #pragma unroll
@@ -259,24 +281,24 @@ void step_bf16_kernel(StepBf16Args a) {
     }
   }
 
-  const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.kp) + (size_t)kvh * a.npb * S::TILE;
-  const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.vp) + (size_t)kvh * a.npb * S::TILE;
+  // Key/value tiles of this head: bpad / 64 per head in the slot.
+  const size_t head_tiles = (size_t)(a.bpad / kKeyTile);
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.kp) + (size_t)kvh * head_tiles * S::TILE;
+  const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.vp) + (size_t)kvh * head_tiles * S::TILE;
   auto issue_k = [&](int t) { S::load_tile(kg + (size_t)t * S::TILE, kbuf(t), wave, lane); };
   auto issue_v = [&](int t) { S::load_tile(vg + (size_t)t * S::TILE, vbuf(t), wave, lane); };
 
-  // Every iteration t (pipelined or not) issues K(t+2) and V(t+1); the
-  // prologue issues K(0), V(0), K(1).  At the top of iteration t, K(t), V(t)
-  // and (when it exists) K(t+1) are resident.
-  if (T > 0) {
-    issue_k(0);
-    issue_v(0);
-  }
-  if (T > 1) issue_k(1);
+  // Every iteration t (pipelined or not) issues V(t+2) then K(t+3), and at its
+  // end waits for everything but those (the loads of iteration t-1: V(t+1),
+  // K(t+2)) before the barrier.  The prologue issues K(0..2), V(0..1).  At the
+  // top of iteration t, K(t), K(t+1), K(t+2) and V(t), V(t+1) are resident.
+  for (int i = 0; i < 3 && i < T; ++i) issue_k(i);
+  for (int i = 0; i < 2 && i < T; ++i) issue_v(i);
   wait_all_and_sync();
 
-  f32x16 sa[2], sb[2];
-  float mxa[2], mxb[2];
-  bf16x8 pb[2][2];
+  f32x16 sa[NT], sb[NT];
+  float mxa[NT], mxb[NT];
+  bf16x8 pb[NT][2];
   if (F >= 1) {
     S::scores(sa, kbuf(0), 0, qf, l32, hi);
     S::rowmax(sa, mxa);
@@ -286,8 +308,9 @@ void step_bf16_kernel(StepBf16Args a) {
   // half 0 feed PV; half B: scores of the next tile's half 0 while half 1 does.
   int t = 0;
   for (; t + 1 < F; ++t) {
-    if (t + 2 < T) issue_k(t + 2);
-    issue_v(t + 1);
+    const bool both = t + 3 < T;
+    if (t + 2 < T) issue_v(t + 2);
+    if (t + 3 < T) issue_k(t + 3);
     S::decide(mxa, mref, zs, o, a.sl2);
     S::scores(sb, kbuf(t), 1, qf, l32, hi);
     S::probs(sa, mref, zs, pb, a.sl2);
@@ -298,11 +321,14 @@ void step_bf16_kernel(StepBf16Args a) {
     S::probs(sb, mref, zs, pb, a.sl2);
     S::pv(o, vbuf(t), 1, pb, l32, hi);
     S::rowmax(sa, mxa);
-    wait_all_and_sync();
+    if (both)
+      wait_keep_and_sync<2 * S::PER_WAVE>();
+    else
+      wait_all_and_sync();
   }
   if (t < F) {  // last full tile: no next scores
-    if (t + 2 < T) issue_k(t + 2);
-    if (t + 1 < T) issue_v(t + 1);
+    if (t + 2 < T) issue_v(t + 2);
+    if (t + 3 < T) issue_k(t + 3);
     S::decide(mxa, mref, zs, o, a.sl2);
     S::scores(sb, kbuf(t), 1, qf, l32, hi);
     S::probs(sa, mref, zs, pb, a.sl2);
@@ -318,15 +344,15 @@ void step_bf16_kernel(StepBf16Args a) {
   // Remaining tiles: element masks (causal diagonal, ragged tail) and waves
   // whose rows end earlier than the workgroup's.
   for (; t < T; ++t) {
-    if (t + 2 < T) issue_k(t + 2);
-    if (t + 1 < T) issue_v(t + 1);
+    if (t + 2 < T) issue_v(t + 2);
+    if (t + 3 < T) issue_k(t + 3);
     if (t < my_tiles) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         S::scores(sa, kbuf(t), half, qf, l32, hi);
         if (t >= my_full) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < NT; ++nt) {
             const int qi = q0 + nt * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -349,7 +375,7 @@ void step_bf16_kernel(StepBf16Args a) {
 
   if (a.last) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const float zt = zs[nt] + __shfl_xor(zs[nt], 32);
       const int qi = q0 + nt * 32 + l32;
       if (qi < a.b) {
@@ -372,7 +398,7 @@ void step_bf16_kernel(StepBf16Args a) {
     }
   } else {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       cm[nt * 64 + lane] = mref[nt];
       cz[nt * 64 + lane] = zs[nt];
 #pragma unroll
@@ -387,10 +413,11 @@ void step_bf16_kernel(StepBf16Args a) {
 
 hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st) {
   const unsigned grid = (unsigned)a.wgs_per_head * (unsigned)a.Hkv;
+  const dim3 block(64 * kStepWaves);
   if (D == 128)
-    hipLaunchKernelGGL(step_bf16_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((step_bf16_kernel<128, kStepNT>), dim3(grid), block, 0, st, a);
   else
-    hipLaunchKernelGGL(step_bf16_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((step_bf16_kernel<64, kStepNT>), dim3(grid), block, 0, st, a);
   return hipGetLastError();
 }
 
