@@ -156,9 +156,12 @@ int check_forward_args(const void* q, const void* k, const void* v, const void* 
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-template <typename StepFn, typename HopFn>
-int run_ring(int P, int rank, int causal, int layout, size_t slot_bytes, size_t carry_bytes, hipStream_t st,
-             HopFn hop_into, StepFn step) {
+// Workspace: two key/value slots, then `extra_bytes` for the step kernels'
+// state (init() prepares it once per call).  step(slot, extra, i, shift,
+// carry_in, last, stream) runs visit i.
+template <typename StepFn, typename HopFn, typename InitFn>
+int run_ring(int P, int rank, int causal, int layout, size_t slot_bytes, size_t extra_bytes, hipStream_t st,
+             HopFn hop_into, StepFn step, InitFn init) {
   DeviceCtx* ctx = nullptr;
   int rc = device_ctx(&ctx);
   if (rc != RINGATTN_OK) return rc;
@@ -177,9 +180,9 @@ int run_ring(int P, int rank, int causal, int layout, size_t slot_bytes, size_t 
   hipStream_t hs = serial ? st : ctx->hop;
 
   void* ws = nullptr;
-  HIP_TRY(hipMallocAsync(&ws, 2 * slot_bytes + carry_bytes, st));
+  HIP_TRY(hipMallocAsync(&ws, 2 * slot_bytes + extra_bytes, st));
   char* slot[2] = {static_cast<char*>(ws), static_cast<char*>(ws) + slot_bytes};
-  char* carry = static_cast<char*>(ws) + 2 * slot_bytes;
+  char* extra = static_cast<char*>(ws) + 2 * slot_bytes;
 
   int status = RINGATTN_OK;
   auto run = [&]() -> int {
@@ -187,6 +190,7 @@ int run_ring(int P, int rank, int causal, int layout, size_t slot_bytes, size_t 
       HIP_TRY(hipEventRecord(ctx->ev_start, st));
       HIP_TRY(hipStreamWaitEvent(hs, ctx->ev_start, 0));
     }
+    HIP_TRY(init(extra, st));
     HIP_TRY(hop_into(visits[0].r, slot[0], st));
     if (n > 1) {
       HIP_TRY(hop_into(visits[1].r, slot[1], hs));
@@ -195,7 +199,7 @@ int run_ring(int P, int rank, int causal, int layout, size_t slot_bytes, size_t 
     for (int i = 0; i < n; ++i) {
       if (i > 0 && !serial) HIP_TRY(hipStreamWaitEvent(st, ctx->ev_ready[i & 1], 0));
       const int tix = timing_begin(st, 0);
-      HIP_TRY(step(slot[i & 1], carry, visits[i].shift, i > 0, i == n - 1, st));
+      HIP_TRY(step(slot[i & 1], extra, i, visits[i].shift, i > 0, i == n - 1, st));
       timing_end(tix, st);
       if (i + 2 < n) {
         if (!serial) {
@@ -240,36 +244,52 @@ int ringattn_forward(const void* q, const void* k, const void* v, void* out, flo
   const __bf16* vb = static_cast<const __bf16*>(v);
   const size_t shard_elems = (size_t)b * Hkv * D;
 
+  StepBf16Args a;
+  a.q = static_cast<const __bf16*>(q);
+  a.out = static_cast<__bf16*>(out);
+  a.lse = lse;
+  a.b = b;
+  a.bpad = bpad;
+  a.npb = npb;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.items = G * npb;
+  a.wgs_per_head = (a.items + kStepWaves - 1) / kStepWaves;
+  a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  const int grid = step_bf16_grid(a);
+  // extra: running state A, running state B (steps alternate), flags.
+  const size_t flag_bytes = round_up((size_t)grid * sizeof(int), 256);
+  const size_t extra_bytes = 2 * carry_bytes + flag_bytes;
+
   auto hop = [&](int r, char* slot, hipStream_t s) -> hipError_t {
     __bf16* kp = reinterpret_cast<__bf16*>(slot);
     return launch_pack_bf16(kb + (size_t)r * shard_elems, vb + (size_t)r * shard_elems, kp, kp + kv_elems, b,
                             bpad, Hkv, D, s);
   };
-  auto step = [&](char* slot, char* carry, int shift, bool carry_in, bool last, hipStream_t s) -> hipError_t {
-    StepBf16Args a;
-    a.q = static_cast<const __bf16*>(q);
-    a.kp = reinterpret_cast<const __bf16*>(slot);
-    a.vp = a.kp + kv_elems;
-    a.cy = reinterpret_cast<float*>(carry);
-    a.cm = reinterpret_cast<float*>(carry + cy_bytes);
-    a.cz = reinterpret_cast<float*>(carry + cy_bytes + cmz_bytes);
-    a.out = static_cast<__bf16*>(out);
-    a.lse = lse;
-    a.b = b;
-    a.bpad = bpad;
-    a.npb = npb;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.G = G;
-    a.items = G * npb;
-    a.wgs_per_head = (a.items + kStepWaves - 1) / kStepWaves;
-    a.shift = shift;
-    a.carry_in = carry_in;
-    a.last = last;
-    a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
-    return launch_step_bf16(a, D, s);
+  auto init = [&](char* extra, hipStream_t s) -> hipError_t {
+    return launch_zero_flags(reinterpret_cast<int*>(extra + 2 * carry_bytes), grid, s);
   };
-  return run_ring(P, rank, causal, layout, slot_bytes, carry_bytes, st, hop, step);
+  auto step = [&](char* slot, char* extra, int i, int shift, bool carry_in, bool last, hipStream_t s) -> hipError_t {
+    StepBf16Args x = a;
+    char* cin = extra + (size_t)((i + 1) & 1) * carry_bytes;   // written by step i-1
+    char* cout = extra + (size_t)(i & 1) * carry_bytes;
+    x.kp = reinterpret_cast<const __bf16*>(slot);
+    x.vp = x.kp + kv_elems;
+    x.cy = reinterpret_cast<const float*>(cin);
+    x.cm = reinterpret_cast<const float*>(cin + cy_bytes);
+    x.cz = reinterpret_cast<const float*>(cin + cy_bytes + cmz_bytes);
+    x.cyo = reinterpret_cast<float*>(cout);
+    x.cmo = reinterpret_cast<float*>(cout + cy_bytes);
+    x.czo = reinterpret_cast<float*>(cout + cy_bytes + cmz_bytes);
+    x.flags = reinterpret_cast<int*>(extra + 2 * carry_bytes);
+    x.shift = shift;
+    x.carry_in = carry_in;
+    x.last = last;
+    return launch_step_bf16(x, D, s);
+  };
+  return run_ring(P, rank, causal, layout, slot_bytes, extra_bytes, st, hop, step,
+                  init);
 }
 
 int ringattn_forward_f32(const float* q, const float* k, const float* v, float* out, float* lse, int64_t N, int P,
@@ -292,7 +312,8 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
     return hipMemcpyAsync(slot + half, v + (size_t)r * shard_elems, shard_elems * sizeof(float),
                           hipMemcpyDeviceToDevice, s);
   };
-  auto step = [&](char* slot, char* carry, int shift, bool carry_in, bool last, hipStream_t s) -> hipError_t {
+  auto init = [](char*, hipStream_t) -> hipError_t { return hipSuccess; };
+  auto step = [&](char* slot, char* carry, int, int shift, bool carry_in, bool last, hipStream_t s) -> hipError_t {
     StepF32Args a;
     a.q = q;
     a.k = reinterpret_cast<const float*>(slot);
@@ -312,7 +333,7 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
     a.scale = (float)(1.0 / std::sqrt((double)D));
     return launch_step_f32(a, D, s);
   };
-  return run_ring(P, rank, causal, layout, slot_bytes, carry_bytes, st, hop, step);
+  return run_ring(P, rank, causal, layout, slot_bytes, carry_bytes, st, hop, step, init);
 }
 
 int ringattn_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows, int Hq, int d_h,

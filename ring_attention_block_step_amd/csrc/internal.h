@@ -30,9 +30,13 @@ struct StepBf16Args {
   const __bf16* q;   // [b, Hq, D] caller's query rows
   const __bf16* kp;  // slot keys   [Hkv][bpad/64] tiles of 64 x D, chunk-major (key_tile_off)
   const __bf16* vp;  // slot values [Hkv][bpad/64] tiles of D x 64, transposed, chunk-major (val_tile_off)
-  float* cy;         // running y   [Hq*npb][kStepNT][D/32][16][64]  (register order)
-  float* cm;         // running m   [Hq*npb][kStepNT][64]  (log2 units, scaled)
-  float* cz;         // running z   [Hq*npb][kStepNT][64]  (per-lane partial sums)
+  const float* cy;   // running y in  [Hq*npb][kStepNT][D/32][16][64]  (register order)
+  const float* cm;   // running m in  [Hq*npb][kStepNT][64]  (log2 units, scaled)
+  const float* cz;   // running z in  [Hq*npb][kStepNT][64]  (per-lane partial sums)
+  float* cyo;        // running state out, same layouts (never the input buffers)
+  float* cmo;
+  float* czo;
+  int* flags;        // [gridDim.x] set by the fast kernel for a workgroup that must be redone exactly
   __bf16* out;       // [b, Hq, D]
   float* lse;        // [Hq, b] or null
   int b, bpad, npb, Hq, Hkv, G;
@@ -80,7 +84,12 @@ inline int64_t padded_rows(int64_t b) { return (b + kKeyTile - 1) / kKeyTile * k
 hipError_t launch_pack_bf16(const __bf16* k_shard, const __bf16* v_shard, __bf16* kp, __bf16* vp,
                             int b, int bpad, int Hkv, int D, hipStream_t st);
 
+// The step as two launches: the fast kernel (fixed softmax reference per row,
+// flags workgroups whose probabilities would leave the safe range), then the
+// exact kernel, which returns at once unless its workgroup is flagged.
 hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st);
+hipError_t launch_zero_flags(int* flags, int n, hipStream_t st);
+int step_bf16_grid(const StepBf16Args& a);
 hipError_t launch_step_f32(const StepF32Args& a, int D, hipStream_t st);
 hipError_t launch_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows,
                         int Hq, int D, void* out, int out_f32, float* lse, hipStream_t st);

@@ -27,10 +27,15 @@
 // the ragged tail) run afterwards without the pipeline.
 //
 // Softmax in base 2: scores are scaled by log2(e)/sqrt(d) inside one FMA, and
-// m is kept in those units.  The running reference m is raised only when a
-// tile's maximum exceeds it by more than kLazy (2^8): any common reference
-// cancels in y / z, so skipping the rescale is exact while every probability
-// stays <= 256.  A rescale is therefore rare after the first tiles.
+// m is kept in those units.  The fast kernel keeps one reference m per row for
+// the whole launch (the carried one, or the maximum of the row's first half
+// tile): any common reference cancels in y / z, so this is the same exact
+// recurrence with the rescale factor exp(m_old - m_new) applied to the
+// reference-free sums.  A probability above 2^24 (or a NaN) flags the
+// workgroup, and the exact kernel launched after it recomputes that
+// workgroup from the untouched input state with the running maximum,
+// raising the reference when a maximum exceeds it by more than 2^8 and
+// rescaling y and z by exp2(m_old - m_new).
 #include "internal.h"
 
 namespace ringattn {
@@ -43,6 +48,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_t;
 
 constexpr float kLazy = 8.0f;
+
 constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -159,6 +165,42 @@ struct Step {
     }
   }
 
+  // Fragments of one half tile, read from LDS ahead of the MFMA cluster that
+  // consumes them: kf[ks] = key rows half*32 + l32, d = 16*ks + 8*hi .. +7;
+  // vf[gg][dt] = value rows d = 32*dt + l32, keys of group 2*half + gg.
+  static __device__ __forceinline__ void kfrags(bf16x8 (&kf)[KS], const lds_t* kb, int half, int l32, int hi) {
+    const int row = half * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(kb + key_tile_off(row, ks * 2 + hi));
+  }
+  static __device__ __forceinline__ void vfrags(bf16x8 (&vf)[2][DT], const lds_t* vb, int half, int l32, int hi) {
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        vf[gg][dt] = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
+            vb + val_tile_off<D>(dt * 32 + l32, (half * 2 + gg) * 2 + hi));
+  }
+  static __device__ __forceinline__ void scores_f(f32x16 (&s)[NT], const bf16x8 (&kf)[KS], const bf16x8 (&qf)[NT][KS]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) s[nt] = mfma(kf[ks], qf[nt][ks], s[nt]);
+  }
+  static __device__ __forceinline__ void pv_f(f32x16 (&o)[NT][DT], const bf16x8 (&vf)[2][DT], const bf16x8 (&pb)[NT][2]) {
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma(vf[gg][dt], pb[nt][gg], o[nt][dt]);
+  }
+
   // O^T += V^T P^T for the 32 keys of one half tile (key groups 2*half, 2*half+1).
   static __device__ __forceinline__ void pv(f32x16 (&o)[NT][DT], const lds_t* vb, int half, const bf16x8 (&pb)[NT][2],
                                             int l32, int hi) {
@@ -198,7 +240,10 @@ __device__ __forceinline__ void wait_keep_and_sync() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, int NT>
+// A probability above this (or a NaN) sends the workgroup to the exact kernel.
+constexpr float kSafeSum = 16777216.0f;  // 2^24, bound on a lane's 16 probabilities per half tile
+
+template <int D, int NT, bool EXACT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512 / NT, 512 / NT), amdgpu_waves_per_eu(3 - NT, 3 - NT)))
 void step_bf16_kernel(StepBf16Args a) {
   using S = Step<D, NT>;
@@ -206,6 +251,10 @@ void step_bf16_kernel(StepBf16Args a) {
   constexpr int WAVES = S::WAVES;
   constexpr int DT = S::DT;
   constexpr int KS = S::KS;
+
+  // The exact kernel only redoes workgroups the fast kernel flagged.
+  if (EXACT && a.flags[blockIdx.x] == 0) return;
+
   // Four key buffers (tile t in t % 4) and three value buffers (t % 3):
   // iteration t reads K(t), K(t+1), V(t) while V(t+2) and K(t+3) stream in, so
   // every load has a whole iteration to land before it is waited for.
@@ -237,7 +286,9 @@ void step_bf16_kernel(StepBf16Args a) {
   const int first_item = wgi * WAVES;
   const int last_item = min(first_item + WAVES - 1, a.items - 1);
   const int T = (keys_upto(min((last_item / a.G) * ROWS + ROWS, a.b)) + kKeyTile - 1) / kKeyTile;
-  const int F = min(T, full_upto((first_item / a.G) * ROWS) / kKeyTile);  // pipelined tiles
+  // Tiles every row of the workgroup sees in full run in the fast pipeline;
+  // the exact kernel takes every tile through the per-tile path.
+  const int F = EXACT ? 0 : min(T, full_upto((first_item / a.G) * ROWS) / kKeyTile);
   const int my_tiles = active ? (keys_upto(min(q0 + ROWS, a.b)) + kKeyTile - 1) / kKeyTile : 0;
   const int my_full = full_upto(q0) / kKeyTile;
 
@@ -256,10 +307,11 @@ void step_bf16_kernel(StepBf16Args a) {
   f32x16 o[NT][DT];
   float mref[NT], zs[NT];
   const size_t ig = (size_t)hq * a.npb + pblk;
-  float* cy = a.cy + ig * (size_t)(NT * DT * 16 * 64);
-  float* cm = a.cm + ig * (NT * 64);
-  float* cz = a.cz + ig * (NT * 64);
+  const size_t ystride = (size_t)(NT * DT * 16 * 64);
   if (a.carry_in && active) {
+    const float* cy = a.cy + ig * ystride;
+    const float* cm = a.cm + ig * (NT * 64);
+    const float* cz = a.cz + ig * (NT * 64);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       mref[nt] = cm[nt * 64 + lane];
@@ -288,61 +340,95 @@ void step_bf16_kernel(StepBf16Args a) {
   auto issue_k = [&](int t) { S::load_tile(kg + (size_t)t * S::TILE, kbuf(t), wave, lane); };
   auto issue_v = [&](int t) { S::load_tile(vg + (size_t)t * S::TILE, vbuf(t), wave, lane); };
 
-  // Every iteration t (pipelined or not) issues V(t+2) then K(t+3), and at its
-  // end waits for everything but those (the loads of iteration t-1: V(t+1),
-  // K(t+2)) before the barrier.  The prologue issues K(0..2), V(0..1).  At the
-  // top of iteration t, K(t), K(t+1), K(t+2) and V(t), V(t+1) are resident.
+  // Every iteration t issues V(t+2) and K(t+3), and at its end waits for
+  // everything but those (the loads of iteration t-1: V(t+1), K(t+2)) before
+  // the barrier.  The prologue issues K(0..2), V(0..1).  At the top of
+  // iteration t, K(t), K(t+1), K(t+2) and V(t), V(t+1) are resident.
   for (int i = 0; i < 3 && i < T; ++i) issue_k(i);
   for (int i = 0; i < 2 && i < T; ++i) issue_v(i);
   wait_all_and_sync();
+  if (EXACT && tid == 0) a.flags[blockIdx.x] = 0;  // every thread has read the flag
 
   f32x16 sa[NT], sb[NT];
-  float mxa[NT], mxb[NT];
-  bf16x8 pb[NT][2];
+  float mxa[NT];
+  bf16x8 pb[NT][2], p1[NT][2];
+  bf16x8 kf[KS];
+  bf16x8 vf[2][DT];
+  bool ok = true;
+  int t = 0;
+
   if (F >= 1) {
+    // Fixed reference per row: the carried m, or for a row that has seen no
+    // key yet the maximum of its first half tile.  Any common reference
+    // cancels in y / z, so the recurrence is unchanged; the reference only
+    // has to keep the probabilities in range, which the check below verifies.
     S::scores(sa, kbuf(0), 0, qf, l32, hi);
     S::rowmax(sa, mxa);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      if (mref[nt] == -INFINITY) mref[nt] = mxa[nt] * a.sl2;
+    S::kfrags(kf, kbuf(0), 1, l32, hi);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p1[nt][gg][e] = (__bf16)0.0f;
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[gg][dt][e] = (__bf16)0.0f;
   }
 
-  // Pipelined full tiles.  Half A: scores of half 1 while the probabilities of
-  // half 0 feed PV; half B: scores of the next tile's half 0 while half 1 does.
-  int t = 0;
-  for (; t + 1 < F; ++t) {
+  // Fast pipeline over half tiles.  Block h issues, with no data dependence
+  // between them, the MFMAs of PV(h-1) and S(h+1), the LDS reads of the next
+  // block's fragments (each refilled right after its last MFMA use), and the
+  // VALU softmax of half tile h against the fixed reference.  No branch and no
+  // VALU touch the accumulators y, so the scheduler interleaves the streams.
+  for (; t < F; ++t) {
     const bool both = t + 3 < T;
+    float zt[NT];
+    // block A: PV(t-1, 1), S(t, 1) | V(t).0, K(t+1).0 | probabilities of S(t, 0)
     if (t + 2 < T) issue_v(t + 2);
+    S::pv_f(o, vf, p1);
+    S::scores_f(sb, kf, qf);
+    S::vfrags(vf, vbuf(t), 0, l32, hi);
+    S::kfrags(kf, kbuf(t + 1), 0, l32, hi);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) zt[nt] = 0.f;
+    S::probs(sa, mref, zt, pb, a.sl2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      ok = ok && (zt[nt] <= kSafeSum);
+      zs[nt] += zt[nt];
+    }
+    // block B: PV(t, 0), S(t+1, 0) | V(t).1, K(t+1).1 | probabilities of S(t, 1)
     if (t + 3 < T) issue_k(t + 3);
-    S::decide(mxa, mref, zs, o, a.sl2);
-    S::scores(sb, kbuf(t), 1, qf, l32, hi);
-    S::probs(sa, mref, zs, pb, a.sl2);
-    S::pv(o, vbuf(t), 0, pb, l32, hi);
-    S::rowmax(sb, mxb);
-    S::decide(mxb, mref, zs, o, a.sl2);
-    S::scores(sa, kbuf(t + 1), 0, qf, l32, hi);
-    S::probs(sb, mref, zs, pb, a.sl2);
-    S::pv(o, vbuf(t), 1, pb, l32, hi);
-    S::rowmax(sa, mxa);
+    S::pv_f(o, vf, pb);
+    S::scores_f(sa, kf, qf);
+    S::vfrags(vf, vbuf(t), 1, l32, hi);
+    S::kfrags(kf, kbuf(t + 1), 1, l32, hi);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) zt[nt] = 0.f;
+    S::probs(sb, mref, zt, p1, a.sl2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      ok = ok && (zt[nt] <= kSafeSum);
+      zs[nt] += zt[nt];
+    }
     if (both)
       wait_keep_and_sync<2 * S::PER_WAVE>();
     else
       wait_all_and_sync();
   }
-  if (t < F) {  // last full tile: no next scores
-    if (t + 2 < T) issue_v(t + 2);
-    if (t + 3 < T) issue_k(t + 3);
-    S::decide(mxa, mref, zs, o, a.sl2);
-    S::scores(sb, kbuf(t), 1, qf, l32, hi);
-    S::probs(sa, mref, zs, pb, a.sl2);
-    S::pv(o, vbuf(t), 0, pb, l32, hi);
-    S::rowmax(sb, mxb);
-    S::decide(mxb, mref, zs, o, a.sl2);
-    S::probs(sb, mref, zs, pb, a.sl2);
-    S::pv(o, vbuf(t), 1, pb, l32, hi);
-    wait_all_and_sync();
-    ++t;
-  }
+  if (F > 0) S::pv_f(o, vf, p1);  // PV(F-1, 1)
+  if (!EXACT && __builtin_amdgcn_ballot_w64(!ok) && lane == 0) a.flags[blockIdx.x] = 1;
 
-  // Remaining tiles: element masks (causal diagonal, ragged tail) and waves
-  // whose rows end earlier than the workgroup's.
+  // Remaining tiles, with the exact running-maximum recurrence: element masks
+  // (causal diagonal, ragged tail), waves whose rows end earlier than the
+  // workgroup's, and every tile of the exact kernel.
   for (; t < T; ++t) {
     if (t + 2 < T) issue_v(t + 2);
     if (t + 3 < T) issue_k(t + 3);
@@ -357,8 +443,8 @@ void step_bf16_kernel(StepBf16Args a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = t * kKeyTile + S::key_of(half, r, hi);
-              const bool ok = key < a.b && (a.shift < 0 || key <= qi - a.shift);
-              if (!ok) sa[nt][r] = -INFINITY;
+              const bool okk = key < a.b && (a.shift < 0 || key <= qi - a.shift);
+              if (!okk) sa[nt][r] = -INFINITY;
             }
           }
         }
@@ -397,6 +483,9 @@ void step_bf16_kernel(StepBf16Args a) {
       }
     }
   } else {
+    float* cy = a.cyo + ig * ystride;
+    float* cm = a.cmo + ig * (NT * 64);
+    float* cz = a.czo + ig * (NT * 64);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       cm[nt * 64 + lane] = mref[nt];
@@ -409,15 +498,31 @@ void step_bf16_kernel(StepBf16Args a) {
   }
 }
 
+__global__ void zero_flags_kernel(int* flags, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) flags[i] = 0;
+}
+
 }  // namespace
 
+int step_bf16_grid(const StepBf16Args& a) { return a.wgs_per_head * a.Hkv; }
+
 hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st) {
-  const unsigned grid = (unsigned)a.wgs_per_head * (unsigned)a.Hkv;
+  const dim3 grid((unsigned)step_bf16_grid(a));
   const dim3 block(64 * kStepWaves);
-  if (D == 128)
-    hipLaunchKernelGGL((step_bf16_kernel<128, kStepNT>), dim3(grid), block, 0, st, a);
-  else
-    hipLaunchKernelGGL((step_bf16_kernel<64, kStepNT>), dim3(grid), block, 0, st, a);
+  if (D == 128) {
+    hipLaunchKernelGGL((step_bf16_kernel<128, kStepNT, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((step_bf16_kernel<128, kStepNT, true>), grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((step_bf16_kernel<64, kStepNT, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((step_bf16_kernel<64, kStepNT, true>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_flags(int* flags, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_flags_kernel, dim3((n + 255) / 256), dim3(256), 0, st, flags, n);
   return hipGetLastError();
 }
 

@@ -144,6 +144,39 @@ def test_equal_keys_give_mean_of_allowed_values():
                 assert np.abs(lse.cpu().numpy()[h] - (s0 + np.log(tq + 1))).max() <= 1e-3
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("boost", [0.35, 3.0])
+def test_late_dominant_key(layout, boost):
+    """One key, late in the sequence, scores far above everything before it.
+    With boost 3.0 every query's score for it exceeds the first tile's maximum
+    by ~40 (log2 units), beyond the fixed-reference range, so the exact
+    recomputation has to take over; with 0.35 the growth (~5) stays in range.
+    Both must match the oracle."""
+    N, P, Hq, Hkv, d = 1024, 4, 4, 2, 128
+    g = torch.Generator().manual_seed(31)
+    q_glob = torch.randn(N, Hq, d, generator=g).abs().to(torch.bfloat16)
+    k_glob = torch.randn(N, Hkv, d, generator=g)
+    star = 700
+    k_glob[star] = boost
+    k_glob = k_glob.to(torch.bfloat16)
+    v_glob = torch.randn(N, Hkv, d, generator=g).to(torch.bfloat16)
+    b = N // P
+    kq = ra.pack_shards(k_glob, P, layout).cuda()
+    vq = ra.pack_shards(v_glob, P, layout).cuda()
+    for rank in range(P):
+        q = q_glob[ra.shard_index(N, P, layout, rank)].cuda()
+        for _ in range(2):   # the second call must not see stale flags
+            out, lse = ra.forward(q, kq, vq, P=P, rank=rank, causal=True, layout=layout)
+        torch.cuda.synchronize()
+        tq = oracle.shard_positions(layout, rank, P, b)
+        want_o, want_lse = oracle.dense_attention(q_glob[tq].double().numpy(), tq, k_glob.double().numpy(),
+                                                  v_glob.double().numpy(), True)
+        w = _w("late-key", N=N, P=P, ranks=(rank,), layout=layout, Hq=Hq, Hkv=Hkv, d=d)
+        stats = compare(w, out.float().cpu().numpy(), lse.cpu().numpy(), want_o, want_lse)
+        print(f"[gpu] late-key boost={boost} {layout} rank={rank} -> {stats}", flush=True)
+        check(w, stats)
+
+
 def test_serial_and_overlapped_hops_are_bit_identical():
     """The double buffer on the second stream must not race: outputs with the hop
     copies serialised on the caller stream are bit-identical."""
