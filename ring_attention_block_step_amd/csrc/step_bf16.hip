@@ -20,22 +20,23 @@
 // chunk-major so the fragment reads are conflict-free and need no per-lane
 // address arithmetic.
 //
-// Software pipeline over the tiles every row of the workgroup sees in full:
-// iteration t issues the MFMAs of S(t+1) while the VALU computes the
-// probabilities of tile t, then the MFMAs of PV(t) while the VALU reduces the
-// row maxima of S(t+1).  Tiles that need an element mask (the causal diagonal,
-// the ragged tail) run afterwards without the pipeline.
+// Software pipeline over the tiles every row of the workgroup sees in full,
+// in half tiles of 32 keys: block h issues the MFMAs of PV(h-1) and S(h+1)
+// while the VALU turns S(h) into probabilities, and the LDS reads of the next
+// block's fragments slot in between (a fixed MFMA / LDS / VALU issue pattern).
+// The loop body has no branch.  Tiles that need an element mask (the causal
+// diagonal, the ragged tail) run afterwards without the pipeline.
 //
 // Softmax in base 2: scores are scaled by log2(e)/sqrt(d) inside one FMA, and
 // m is kept in those units.  The fast kernel keeps one reference m per row for
 // the whole launch (the carried one, or the maximum of the row's first half
 // tile): any common reference cancels in y / z, so this is the same exact
 // recurrence with the rescale factor exp(m_old - m_new) applied to the
-// reference-free sums.  A probability above 2^24 (or a NaN) flags the
-// workgroup, and the exact kernel launched after it recomputes that
-// workgroup from the untouched input state with the running maximum,
-// raising the reference when a maximum exceeds it by more than 2^8 and
-// rescaling y and z by exp2(m_old - m_new).
+// reference-free sums.  When a lane's 16 probabilities of a half tile sum to
+// more than 2^24 (or to a NaN) the workgroup is flagged, and the exact kernel
+// launched after it recomputes that workgroup from the untouched input state
+// with the running maximum, raising the reference when a maximum exceeds it
+// by more than 8 (a factor 2^8) and rescaling y and z by exp2(m_old - m_new).
 #include "internal.h"
 
 namespace ringattn {
@@ -240,6 +241,23 @@ __device__ __forceinline__ void wait_keep_and_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Issue order of one half-tile block of the fast loop: the block's 16*NT
+// MFMAs are spread evenly, each followed by three VALU/transcendental ops of
+// the softmax, with the block's 16 LDS fragment reads placed between them, so
+// a wave keeps the matrix pipe fed while its vector ALU works (left alone,
+// the scheduler bunches the MFMAs, then the reads, then the VALU).
+// Scheduling-group masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU, 0x400 TRANS.
+template <int NT>
+__device__ __forceinline__ void interleave_block() {
+#pragma unroll
+  for (int i = 0; i < 16 * NT; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i % NT == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // A probability above this (or a NaN) sends the workgroup to the exact kernel.
 constexpr float kSafeSum = 16777216.0f;  // 2^24, bound on a lane's 16 probabilities per half tile
 
@@ -337,8 +355,11 @@ void step_bf16_kernel(StepBf16Args a) {
   const size_t head_tiles = (size_t)(a.bpad / kKeyTile);
   const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.kp) + (size_t)kvh * head_tiles * S::TILE;
   const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.vp) + (size_t)kvh * head_tiles * S::TILE;
-  auto issue_k = [&](int t) { S::load_tile(kg + (size_t)t * S::TILE, kbuf(t), wave, lane); };
-  auto issue_v = [&](int t) { S::load_tile(vg + (size_t)t * S::TILE, vbuf(t), wave, lane); };
+  // Tile t lands in buffer kbuf(t) / vbuf(t).  The source index is clamped to
+  // the last tile, so a prefetch past the end reads valid memory into a buffer
+  // that no later iteration reads.
+  auto issue_k = [&](int t) { S::load_tile(kg + (size_t)min(t, T - 1) * S::TILE, kbuf(t), wave, lane); };
+  auto issue_v = [&](int t) { S::load_tile(vg + (size_t)min(t, T - 1) * S::TILE, vbuf(t), wave, lane); };
 
   // Every iteration t issues V(t+2) and K(t+3), and at its end waits for
   // everything but those (the loads of iteration t-1: V(t+1), K(t+2)) before
@@ -388,10 +409,12 @@ void step_bf16_kernel(StepBf16Args a) {
   // VALU softmax of half tile h against the fixed reference.  No branch and no
   // VALU touch the accumulators y, so the scheduler interleaves the streams.
   for (; t < F; ++t) {
-    const bool both = t + 3 < T;
     float zt[NT];
+    // Prefetches are unconditional so the loop body is one basic block; past
+    // the last tile they fill a buffer no later iteration reads (V(t+2)
+    // shares its buffer with V(t-1), K(t+3) with K(t-1)).
     // block A: PV(t-1, 1), S(t, 1) | V(t).0, K(t+1).0 | probabilities of S(t, 0)
-    if (t + 2 < T) issue_v(t + 2);
+    issue_v(t + 2);
     S::pv_f(o, vf, p1);
     S::scores_f(sb, kf, qf);
     S::vfrags(vf, vbuf(t), 0, l32, hi);
@@ -404,8 +427,9 @@ void step_bf16_kernel(StepBf16Args a) {
       ok = ok && (zt[nt] <= kSafeSum);
       zs[nt] += zt[nt];
     }
+    interleave_block<NT>();
     // block B: PV(t, 0), S(t+1, 0) | V(t).1, K(t+1).1 | probabilities of S(t, 1)
-    if (t + 3 < T) issue_k(t + 3);
+    issue_k(t + 3);
     S::pv_f(o, vf, pb);
     S::scores_f(sa, kf, qf);
     S::vfrags(vf, vbuf(t), 1, l32, hi);
@@ -418,10 +442,8 @@ void step_bf16_kernel(StepBf16Args a) {
       ok = ok && (zt[nt] <= kSafeSum);
       zs[nt] += zt[nt];
     }
-    if (both)
-      wait_keep_and_sync<2 * S::PER_WAVE>();
-    else
-      wait_all_and_sync();
+    interleave_block<NT>();
+    wait_keep_and_sync<2 * S::PER_WAVE>();
   }
   if (F > 0) S::pv_f(o, vf, p1);  // PV(F-1, 1)
   if (!EXACT && __builtin_amdgcn_ballot_w64(!ok) && lane == 0) a.flags[blockIdx.x] = 1;
