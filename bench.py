@@ -48,7 +48,9 @@ def useful_pairs(layout: str, u: int, P: int, b: int, causal: bool) -> int:
     are fully masked: u*b^2 + b(b+1)/2.  Causal, striped shards (token t on
     device t mod P): local key j of block r may be seen by local query i iff
     j <= i when r <= u and j < i when r > u, so blocks r <= u give b(b+1)/2 and
-    blocks r > u give b(b-1)/2: P*b(b-1)/2 + (u+1)*b.
+    blocks r > u give b(b-1)/2: P*b(b-1)/2 + (u+1)*b.  Causal, zigzag shards
+    (chunks u and 2P-1-u of c = b/2 tokens): each chunk sees every earlier
+    chunk in full and its own lower triangle, (2P-1)*c^2 + c(c+1) on every rank.
     """
     if not causal:
         return P * b * b
@@ -56,6 +58,9 @@ def useful_pairs(layout: str, u: int, P: int, b: int, causal: bool) -> int:
         return u * b * b + b * (b + 1) // 2
     if layout == "striped":
         return P * b * (b - 1) // 2 + (u + 1) * b
+    if layout == "zigzag":
+        c = b // 2
+        return (2 * P - 1) * c * c + c * (c + 1)
     raise ValueError(layout)
 
 

@@ -37,12 +37,25 @@ def shard_positions(layout: str, r: int, P: int, b: int) -> np.ndarray:
     striped: token t lives on device t mod P, so local row j of shard r is
       token j*P + r ("Ring Attention" (aarnphm.xyz): Striped Attention keeps the
       ring schedule but alternates shard ownership).
+    zigzag: the sequence is cut into 2P chunks of c = b/2 tokens and shard r
+      holds chunk r, then chunk 2P-1-r: local row j < c is token r*c + j and
+      local row j >= c is token (2P-1-r)*c + (j - c) ("Ring Attention"
+      (darshanfofadiya.com) 4.8.3, the zigzag assignment table: each GPU gets
+      one early and one late block; transformer-math page, "Causal masking
+      wastes half the ring": device i gets chunks i and 2P-1-i).  Requires an
+      even b.
     """
     j = np.arange(b, dtype=np.int64)
     if layout == "contiguous":
         return r * b + j
     if layout == "striped":
         return j * P + r
+    if layout == "zigzag":
+        if b % 2:
+            raise ValueError("zigzag needs an even shard size")
+        c = b // 2
+        early = j < c
+        return np.where(early, r * c + j, (2 * P - 1 - r) * c + (j - c))
     raise ValueError(f"unknown layout {layout!r}")
 
 

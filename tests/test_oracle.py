@@ -93,6 +93,10 @@ RING_CASES = [
     ("striped", True, 8, 6, 4, 2, 8),
     ("striped", False, 4, 5, 3, 1, 4),
     ("contiguous", True, 2, 16, 6, 3, 32),
+    ("zigzag", True, 4, 6, 4, 2, 8),
+    ("zigzag", True, 8, 4, 2, 1, 4),
+    ("zigzag", False, 2, 8, 2, 1, 8),
+    ("zigzag", True, 1, 10, 2, 1, 8),
 ]
 
 
@@ -110,7 +114,7 @@ def test_ring_equals_dense(layout, causal, P, b, Hq, Hkv, d):
 
 
 @pytest.mark.parametrize("layout,causal", [("contiguous", True), ("striped", True),
-                                           ("contiguous", False)])
+                                           ("contiguous", False), ("zigzag", True)])
 def test_order_invariance(layout, causal):
     rng = np.random.default_rng(7)
     P, b, Hq, Hkv, d = 8, 6, 4, 2, 8
@@ -248,7 +252,8 @@ def _brute_force_row(qv, K, V, allowed, d):
 
 
 @pytest.mark.parametrize("layout,causal,P", [("contiguous", True, 4), ("striped", True, 4),
-                                             ("contiguous", False, 2), ("striped", True, 8)])
+                                             ("contiguous", False, 2), ("striped", True, 8),
+                                             ("zigzag", True, 4), ("zigzag", True, 2)])
 def test_brute_force_tiny(layout, causal, P):
     rng = np.random.default_rng(13 + P)
     N, d = 16, 3
@@ -262,8 +267,11 @@ def test_brute_force_tiny(layout, causal, P):
         # positions written out by hand, independent of shard_positions
         if layout == "contiguous":
             tq = list(range(u * b, u * b + b))
-        else:
+        elif layout == "striped":
             tq = [t for t in range(N) if t % P == u]
+        else:   # zigzag: chunks of b/2 tokens, chunk u then chunk 2P-1-u
+            c = b // 2
+            tq = list(range(u * c, u * c + c)) + list(range((2 * P - 1 - u) * c, (2 * P - u) * c))
         o, lse = ro.ring_forward(q[tq], u, k, v, P, layout, causal)
         o_d, lse_d = ro.dense_attention(q[tq], np.array(tq), k, v, causal)
         for i, t in enumerate(tq):
@@ -292,6 +300,73 @@ def test_shard_positions(P, b):
     assert sorted(seen) == list(range(N))
 
 
+@pytest.mark.parametrize("P,c", [(1, 3), (2, 1), (4, 3), (8, 5)])
+def test_zigzag_positions(P, c):
+    """Shard r holds chunk r, then chunk 2P-1-r, each in token order; the
+    shards together hold every token once."""
+    b, N = 2 * c, 2 * P * c
+    seen = []
+    for r in range(P):
+        z = ro.shard_positions("zigzag", r, P, b).tolist()
+        assert z[:c] == list(range(r * c, (r + 1) * c))
+        assert z[c:] == list(range((2 * P - 1 - r) * c, (2 * P - r) * c))
+        seen.extend(z)
+    assert sorted(seen) == list(range(N))
+    with pytest.raises(ValueError):
+        ro.shard_positions("zigzag", 0, P, b + 1)
+
+
+def _chunk_interactions(P, c, u):
+    """For each chunk that zigzag shard u holds (early, then late): the number
+    of the 2P chunks of keys it has at least one allowed pair with, from the
+    oracle's positions and causal mask."""
+    b = 2 * c
+    tq = ro.shard_positions("zigzag", u, P, b)
+    per = []
+    for half in (tq[:c], tq[c:]):
+        n = 0
+        for ck in range(2 * P):
+            tk = np.arange(ck * c, (ck + 1) * c)
+            n += bool(ro.allowed_mask(half, tk, True).any())
+        per.append(n)
+    return per
+
+
+def test_zigzag_balance_matches_page():
+    g = _load("zigzag_balance.json")
+    P, c = g["P"], 3
+    held, per_chunk, per_gpu = [], [], []
+    for u in range(P):
+        tq = ro.shard_positions("zigzag", u, P, 2 * c)
+        held.append(sorted({int(t) // c for t in tq}))
+        pc = _chunk_interactions(P, c, u)
+        per_chunk.append(pc)
+        per_gpu.append(sum(pc))
+    assert held == g["assignment"]
+    assert per_chunk == g["per_chunk_interactions"]
+    assert per_gpu == g["small_block_interactions_per_gpu"]
+    assert sum(per_gpu) == g["total_small_interactions"]
+    assert per_gpu[0] / 4 == g["big_block_equivalents_per_gpu"]
+    # the contiguous bottleneck from the oracle's own masks
+    worst = max(sum(bool(ro.allowed_mask(ro.shard_positions("contiguous", u, P, c),
+                                         ro.shard_positions("contiguous", r, P, c), True).any())
+                    for r in range(P)) for u in range(P))
+    assert worst == g["contiguous_bottleneck_big_blocks"]
+
+
+def test_zigzag_speedup_matches_page():
+    """Every rank carries 2P+1 small-block interactions, so the wall-clock gain
+    over contiguous shards (P big blocks on the last rank) is P / ((2P+1)/4);
+    the page prints it to two decimals for 8 .. 64 GPUs."""
+    g = _load("zigzag_balance.json")
+    for ps, want in g["speedup_by_gpus"].items():
+        P = int(ps)
+        ranks = range(P) if P <= 16 else (0, P // 2, P - 1)
+        counts = {sum(_chunk_interactions(P, 1, u)) for u in ranks}
+        assert counts == {2 * P + 1}
+        assert round(P / ((2 * P + 1) / 4), g["speedup_decimals"]) == want
+
+
 def test_causal_block_counts_match_page():
     g = _load("causal_block_counts.json")
     P, b = g["P"], 3
@@ -317,6 +392,21 @@ def test_pair_count_closed_forms(P, b):
             bench.useful_pairs("striped", u, P, b, True) == P * b * (b - 1) // 2 + (u + 1) * b
         assert ro.allowed_pair_count("striped", u, P, b, False) == \
             bench.useful_pairs("striped", u, P, b, False) == P * b * b
+
+
+@pytest.mark.parametrize("P,c", [(1, 3), (2, 4), (4, 3), (8, 2)])
+def test_zigzag_pair_count_closed_form(P, c):
+    """Zigzag rank u: chunk u sees u full chunks and its own triangle, chunk
+    2P-1-u sees 2P-1-u full chunks and its triangle: (2P-1) c^2 + c (c+1)
+    pairs, the same on every rank."""
+    import bench
+    b = 2 * c
+    for u in range(P):
+        want = (2 * P - 1) * c * c + c * (c + 1)
+        assert ro.allowed_pair_count("zigzag", u, P, b, True) == \
+            bench.useful_pairs("zigzag", u, P, b, True) == want
+        assert ro.allowed_pair_count("zigzag", u, P, b, False) == \
+            bench.useful_pairs("zigzag", u, P, b, False) == P * b * b
 
 
 def test_bandwidth_budget_figures():
@@ -360,12 +450,12 @@ def _block_partials(q_local, u, k, v, P, layout, causal):
     return np.stack(ms), np.stack(zs), np.stack(ys)
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 def test_merge_of_block_partials_equals_dense(layout):
     rng = np.random.default_rng(21)
     P, b, Hq, Hkv, d = 4, 6, 2, 1, 8
     q, k, v = _rand_qkv(rng, P * b, Hq, Hkv, d, scale=2.0)
-    u = 1 if layout == "striped" else 2   # contiguous rank 2 has fully masked blocks 3
+    u = 2 if layout == "contiguous" else 1   # contiguous rank 2 has fully masked block 3
     tq = ro.shard_positions(layout, u, P, b)
     m, z, y = _block_partials(q[tq], u, k, v, P, layout, True)
     o, lse = ro.merge_partials(m, z, y)
@@ -468,6 +558,16 @@ def _striped_transposed(layout, r, P, b):
     return r * b + j
 
 
+def _zigzag_off_by_one(layout, r, P, b):
+    j = np.arange(b, dtype=np.int64)
+    if layout == "zigzag":
+        c = b // 2
+        return np.where(j < c, r * c + j, (2 * P - 2 - r) * c + (j - c))   # wrong late chunk
+    if layout == "striped":
+        return j * P + r
+    return r * b + j
+
+
 def _pins_fail():
     """Run a representative set of pins; return True if any of them fails."""
     checks = [test_worked_example_outputs_and_trace, test_p1_is_library_softmax_attention,
@@ -477,7 +577,9 @@ def _pins_fail():
     checks += [lambda: test_shard_positions(4, 3),
                lambda: test_brute_force_tiny("striped", True, 4),
                lambda: test_all_equal_keys_give_mean_of_allowed_values("contiguous", True),
-               lambda: test_ring_equals_dense(*RING_CASES[3])]
+               lambda: test_ring_equals_dense(*RING_CASES[3]),
+               lambda: test_brute_force_tiny("zigzag", True, 4),
+               test_zigzag_balance_matches_page]
     for c in checks:
         try:
             with np.errstate(all="ignore"):
@@ -493,6 +595,7 @@ def _pins_fail():
     ("online_fold", _fold_rescale_y_only),
     ("allowed_mask", _exclusive_mask),
     ("shard_positions", _striped_transposed),
+    ("shard_positions", _zigzag_off_by_one),
 ])
 def test_planted_mistakes_are_caught(monkeypatch, target, replacement):
     assert not _pins_fail()
