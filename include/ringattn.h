@@ -40,7 +40,7 @@ enum {
   RINGATTN_EHIP = 3          /* the HIP runtime reported an error (message has the detail) */
 };
 
-enum { RINGATTN_LAYOUT_CONTIGUOUS = 0, RINGATTN_LAYOUT_STRIPED = 1 };
+enum { RINGATTN_LAYOUT_CONTIGUOUS = 0, RINGATTN_LAYOUT_STRIPED = 1, RINGATTN_LAYOUT_ZIGZAG = 2 };
 
 /*
  * ringattn_forward -- rank `rank`'s share of the ring, bf16 in and out.
@@ -49,7 +49,12 @@ enum { RINGATTN_LAYOUT_CONTIGUOUS = 0, RINGATTN_LAYOUT_STRIPED = 1 };
  * b = N / P tokens.  CONTIGUOUS: shard r holds tokens r*b .. r*b+b-1 (the
  * transformer-math page, "The mechanism, compressed").  STRIPED: token t lives
  * on shard t mod P, so local row j of shard r is token j*P + r ("Ring
- * Attention" (aarnphm.xyz): striped ownership balances causal work).
+ * Attention" (aarnphm.xyz): striped ownership balances causal work).  ZIGZAG:
+ * the sequence is cut into 2P chunks of c = b/2 tokens and shard r holds chunk
+ * r followed by chunk 2P-1-r, so local row j < c is token r*c + j and row
+ * j >= c is token (2P-1-r)*c + j - c ("Ring Attention" (darshanfofadiya.com),
+ * 4.8.3: one early and one late block per GPU gives every GPU the same causal
+ * work).
  * Causal (causal = 1): a query attends to keys at GLOBAL token positions <= its
  * own ("Ring Attention" (darshanfofadiya.com), 4.8 and 4.8.1).
  *
@@ -59,11 +64,12 @@ enum { RINGATTN_LAYOUT_CONTIGUOUS = 0, RINGATTN_LAYOUT_STRIPED = 1 };
  *                           Shard `rank` is the device's own block.
  *  out  [b, Hq, d_h]        bf16, O (written)
  *  lse  [Hq, b]             fp32, natural-log LSE (written), may be NULL
- *  N, P, rank               N % P == 0, N >= P >= 1, 0 <= rank < P
+ *  N, P, rank               N % P == 0 (N % 2P == 0 for ZIGZAG), N >= P >= 1,
+ *                           0 <= rank < P
  *  Hq, Hkv                  Hq % Hkv == 0
  *  d_h                      64 or 128
  *  causal                   0 or 1
- *  layout                   RINGATTN_LAYOUT_CONTIGUOUS or _STRIPED
+ *  layout                   RINGATTN_LAYOUT_CONTIGUOUS, _STRIPED or _ZIGZAG
  *
  * The library allocates its workspace (two key/value slots and the fp32 running
  * state) stream-ordered on `stream` and frees it the same way.  The block for

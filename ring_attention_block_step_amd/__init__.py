@@ -21,7 +21,7 @@ __all__ = ["forward", "merge", "shard_index", "pack_shards", "lib", "RingAttnErr
            "timing_enable", "timing_collect", "set_serial_hops", "version", "SYMBOLS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
-LAYOUTS = {"contiguous": 0, "striped": 1}
+LAYOUTS = {"contiguous": 0, "striped": 1, "zigzag": 2}
 
 # Every symbol include/ringattn.h declares.
 SYMBOLS = ("ringattn_forward", "ringattn_forward_f32", "ringattn_merge", "ringattn_status_string",
@@ -102,6 +102,10 @@ def shard_index(N: int, P: int, layout: str, r: int) -> torch.Tensor:
         return grid.view(P, b)[r].clone()
     if layout == "striped":
         return grid.view(b, P)[:, r].clone()
+    if layout == "zigzag":
+        _need(N % (2 * P) == 0, "zigzag needs N to be a multiple of 2P")
+        chunks = grid.view(2 * P, b // 2)
+        return torch.cat([chunks[r], chunks[2 * P - 1 - r]])
     raise ValueError(f"unknown layout {layout!r}")
 
 
@@ -114,6 +118,11 @@ def pack_shards(x: torch.Tensor, P: int, layout: str) -> torch.Tensor:
         return x.reshape(P, b, *x.shape[1:]).contiguous()
     if layout == "striped":
         return x.reshape(b, P, *x.shape[1:]).transpose(0, 1).contiguous()
+    if layout == "zigzag":
+        _need(N % (2 * P) == 0, "zigzag needs N to be a multiple of 2P")
+        chunks = x.reshape(2 * P, b // 2, *x.shape[1:])
+        early, late = chunks[:P], chunks[P:].flip(0)   # shard r: chunk r, then chunk 2P-1-r
+        return torch.stack([early, late], dim=1).reshape(P, b, *x.shape[1:]).contiguous()
     raise ValueError(f"unknown layout {layout!r}")
 
 

@@ -118,18 +118,35 @@ void timing_end(int idx, hipStream_t st) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Mask of visiting block r for rank u; returns false if the block is fully masked.
-bool block_mask(int causal, int layout, int r, int u, int* shift) {
-  if (!causal) {
-    *shift = kMaskNone;
+// Mask of visiting block r for rank u with b rows per shard; returns false if
+// the block is fully masked (it is then never visited).
+bool block_mask(int causal, int layout, int r, int u, int b, BlockMask* mk) {
+  mk->shift = kMaskNone;
+  mk->kend = b;
+  mk->qbeg = 0;
+  if (!causal) return true;
+  if (layout == RINGATTN_LAYOUT_CONTIGUOUS) {
+    if (r > u) return false;
+    if (r == u) mk->shift = 0;
     return true;
   }
-  if (layout == RINGATTN_LAYOUT_CONTIGUOUS) {
-    if (r < u) { *shift = kMaskNone; return true; }
-    if (r == u) { *shift = 0; return true; }
-    return false;
+  if (layout == RINGATTN_LAYOUT_STRIPED) {
+    mk->shift = (r <= u) ? 0 : 1;
+    return true;
   }
-  *shift = (r <= u) ? 0 : 1;
+  // Zigzag: query chunks u (rows < c) and 2P-1-u (rows >= c) against key
+  // chunks r (keys < c) and 2P-1-r (keys >= c).  r == u: each chunk sees the
+  // earlier chunk in full and itself causally, i.e. j <= i.  r < u: both query
+  // chunks see key chunk r in full and not key chunk 2P-1-r > 2P-1-u > u.
+  // r > u: query chunk u sees neither key chunk (both lie later); query chunk
+  // 2P-1-u sees both (r < P <= 2P-1-u and 2P-1-r < 2P-1-u).
+  const int c = b / 2;
+  if (r == u)
+    mk->shift = 0;
+  else if (r < u)
+    mk->kend = c;
+  else
+    mk->qbeg = c;
   return true;
 }
 
@@ -145,8 +162,10 @@ int check_forward_args(const void* q, const void* k, const void* v, const void* 
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
     return fail(RINGATTN_EINVAL, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (got %d, %d)", Hq, Hkv);
   if (causal != 0 && causal != 1) return fail(RINGATTN_EINVAL, "causal must be 0 or 1");
-  if (layout != RINGATTN_LAYOUT_CONTIGUOUS && layout != RINGATTN_LAYOUT_STRIPED)
-    return fail(RINGATTN_EINVAL, "layout must be 0 (contiguous) or 1 (striped)");
+  if (layout != RINGATTN_LAYOUT_CONTIGUOUS && layout != RINGATTN_LAYOUT_STRIPED && layout != RINGATTN_LAYOUT_ZIGZAG)
+    return fail(RINGATTN_EINVAL, "layout must be 0 (contiguous), 1 (striped) or 2 (zigzag)");
+  if (layout == RINGATTN_LAYOUT_ZIGZAG && N % (2 * (int64_t)P) != 0)
+    return fail(RINGATTN_EINVAL, "zigzag needs N (%lld) to be a multiple of 2P (%d)", (long long)N, 2 * P);
   if (d_h != 64 && d_h != 128) return fail(RINGATTN_EUNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
   const int64_t b = N / P;
   if (b > (int64_t)1 << 28 || (int64_t)Hq * b > ((int64_t)1 << 31) / 64)
@@ -157,21 +176,21 @@ int check_forward_args(const void* q, const void* k, const void* v, const void* 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: two key/value slots, then `extra_bytes` for the step kernels'
-// state (init() prepares it once per call).  step(slot, extra, i, shift,
+// state (init() prepares it once per call).  step(slot, extra, i, mask,
 // carry_in, last, stream) runs visit i.
 template <typename StepFn, typename HopFn, typename InitFn>
-int run_ring(int P, int rank, int causal, int layout, size_t slot_bytes, size_t extra_bytes, hipStream_t st,
+int run_ring(int P, int rank, int b, int causal, int layout, size_t slot_bytes, size_t extra_bytes, hipStream_t st,
              HopFn hop_into, StepFn step, InitFn init) {
   DeviceCtx* ctx = nullptr;
   int rc = device_ctx(&ctx);
   if (rc != RINGATTN_OK) return rc;
 
-  struct Visit { int r, shift; };
+  struct Visit { int r; BlockMask mask; };
   std::vector<Visit> visits;
   for (int s = 0; s < P; ++s) {
     const int r = ((rank - s) % P + P) % P;
-    int shift;
-    if (block_mask(causal, layout, r, rank, &shift)) visits.push_back({r, shift});
+    BlockMask mk;
+    if (block_mask(causal, layout, r, rank, b, &mk)) visits.push_back({r, mk});
   }
   const int n = (int)visits.size();  // >= 1: the own block is never fully masked
 
@@ -199,7 +218,7 @@ int run_ring(int P, int rank, int causal, int layout, size_t slot_bytes, size_t 
     for (int i = 0; i < n; ++i) {
       if (i > 0 && !serial) HIP_TRY(hipStreamWaitEvent(st, ctx->ev_ready[i & 1], 0));
       const int tix = timing_begin(st, 0);
-      HIP_TRY(step(slot[i & 1], extra, i, visits[i].shift, i > 0, i == n - 1, st));
+      HIP_TRY(step(slot[i & 1], extra, i, visits[i].mask, i > 0, i == n - 1, st));
       timing_end(tix, st);
       if (i + 2 < n) {
         if (!serial) {
@@ -270,7 +289,8 @@ int ringattn_forward(const void* q, const void* k, const void* v, void* out, flo
   auto init = [&](char* extra, hipStream_t s) -> hipError_t {
     return launch_zero_flags(reinterpret_cast<int*>(extra + 2 * carry_bytes), grid, s);
   };
-  auto step = [&](char* slot, char* extra, int i, int shift, bool carry_in, bool last, hipStream_t s) -> hipError_t {
+  auto step = [&](char* slot, char* extra, int i, const BlockMask& mk, bool carry_in, bool last,
+                  hipStream_t s) -> hipError_t {
     StepBf16Args x = a;
     char* cin = extra + (size_t)((i + 1) & 1) * carry_bytes;   // written by step i-1
     char* cout = extra + (size_t)(i & 1) * carry_bytes;
@@ -283,13 +303,14 @@ int ringattn_forward(const void* q, const void* k, const void* v, void* out, flo
     x.cmo = reinterpret_cast<float*>(cout + cy_bytes);
     x.czo = reinterpret_cast<float*>(cout + cy_bytes + cmz_bytes);
     x.flags = reinterpret_cast<int*>(extra + 2 * carry_bytes);
-    x.shift = shift;
+    x.shift = mk.shift;
+    x.kend = mk.kend;
+    x.qbeg = mk.qbeg;
     x.carry_in = carry_in;
     x.last = last;
     return launch_step_bf16(x, D, s);
   };
-  return run_ring(P, rank, causal, layout, slot_bytes, extra_bytes, st, hop, step,
-                  init);
+  return run_ring(P, rank, b, causal, layout, slot_bytes, extra_bytes, st, hop, step, init);
 }
 
 int ringattn_forward_f32(const float* q, const float* k, const float* v, float* out, float* lse, int64_t N, int P,
@@ -313,7 +334,8 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
                           hipMemcpyDeviceToDevice, s);
   };
   auto init = [](char*, hipStream_t) -> hipError_t { return hipSuccess; };
-  auto step = [&](char* slot, char* carry, int, int shift, bool carry_in, bool last, hipStream_t s) -> hipError_t {
+  auto step = [&](char* slot, char* carry, int, const BlockMask& mk, bool carry_in, bool last,
+                  hipStream_t s) -> hipError_t {
     StepF32Args a;
     a.q = q;
     a.k = reinterpret_cast<const float*>(slot);
@@ -327,13 +349,15 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = Hq / Hkv;
-    a.shift = shift;
+    a.shift = mk.shift;
+    a.kend = mk.kend;
+    a.qbeg = mk.qbeg;
     a.carry_in = carry_in;
     a.last = last;
     a.scale = (float)(1.0 / std::sqrt((double)D));
     return launch_step_f32(a, D, s);
   };
-  return run_ring(P, rank, causal, layout, slot_bytes, carry_bytes, st, hop, step, init);
+  return run_ring(P, rank, b, causal, layout, slot_bytes, carry_bytes, st, hop, step, init);
 }
 
 int ringattn_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows, int Hq, int d_h,

@@ -18,13 +18,22 @@ constexpr int kWaveRows = 32 * kStepNT;
 constexpr int kStepWaves = 8 / kStepNT;
 
 // Mask of one visiting block, in LOCAL row indices (query row i, key row j):
-//   kMaskNone   every key row j < b is allowed;
-//   shift 0     allowed iff j <= i;
-//   shift 1     allowed iff j <  i.
-// Contiguous causal shards give "none" for earlier blocks and shift 0 for the
-// own block (later blocks are fully masked and never launched); striped causal
-// shards give shift 0 for blocks r <= rank and shift 1 for r > rank.
+// key j is allowed for query i iff
+//   j < kend  and  i >= qbeg  and  (shift == kMaskNone  or  j <= i - shift).
+// Contiguous causal shards: earlier blocks are unmasked, the own block has
+// shift 0, later blocks are fully masked (never launched).  Striped causal
+// shards: shift 0 for blocks r <= rank, shift 1 for r > rank.  Zigzag causal
+// shards (chunks r and 2P-1-r of c = b/2 rows): the own block has shift 0,
+// an earlier block r < rank is seen by every row up to key c (kend = c), a
+// later block r > rank is seen in full by rows i >= c only (qbeg = c).
+// Without a causal mask every block is unmasked (kend = b, qbeg = 0).
 constexpr int kMaskNone = -1;
+
+struct BlockMask {
+  int shift;  // kMaskNone, 0 or 1
+  int kend;   // keys j >= kend are masked (kend <= b)
+  int qbeg;   // rows i < qbeg see no key of this block
+};
 
 struct StepBf16Args {
   const __bf16* q;   // [b, Hq, D] caller's query rows
@@ -42,7 +51,9 @@ struct StepBf16Args {
   int b, bpad, npb, Hq, Hkv, G;
   int items;         // query items per key/value head: G * npb
   int wgs_per_head;  // ceil(items / kStepWaves)
-  int shift;         // kMaskNone, 0 or 1
+  int shift;         // block mask (BlockMask)
+  int kend;
+  int qbeg;
   int carry_in;      // read the running state instead of starting empty
   int last;          // finish: write O and LSE instead of the running state
   float sl2;         // log2(e) / sqrt(D)
@@ -58,7 +69,8 @@ struct StepF32Args {
   float* out;        // [b, Hq, D]
   float* lse;        // [Hq, b] or null
   int b, Hq, Hkv, G;
-  int shift, carry_in, last;
+  int shift, kend, qbeg;  // block mask (BlockMask)
+  int carry_in, last;
   float scale;       // 1 / sqrt(D)
 };
 

@@ -297,10 +297,16 @@ void step_bf16_kernel(StepBf16Args a) {
   const int hq = kvh * a.G + it % a.G;
   const int q0 = pblk * ROWS;
 
-  // Tile counts.  Items are ordered row block first, so the first item of the
-  // workgroup has the lowest rows (fewest keys) and the last the highest.
-  auto keys_upto = [&](int qe) { return a.shift < 0 ? a.b : max(0, min(a.b, qe - a.shift)); };
-  auto full_upto = [&](int qlo) { return a.shift < 0 ? a.b : max(0, min(a.b, qlo + 1 - a.shift)); };
+  // Tile counts.  A row i sees the key prefix 0 .. keys_of(i) - 1, and
+  // keys_of is nondecreasing in i, so a row range sees keys_of(last row) keys
+  // at most and keys_of(first row) keys in full.  Items are ordered row block
+  // first, so the first item of the workgroup has the lowest rows (fewest
+  // keys) and the last the highest.
+  auto keys_of = [&](int i) {
+    return i < a.qbeg ? 0 : (a.shift < 0 ? a.kend : max(0, min(a.kend, i + 1 - a.shift)));
+  };
+  auto keys_upto = [&](int qe) { return keys_of(qe - 1); };
+  auto full_upto = [&](int qlo) { return keys_of(qlo); };
   const int first_item = wgi * WAVES;
   const int last_item = min(first_item + WAVES - 1, a.items - 1);
   const int T = (keys_upto(min((last_item / a.G) * ROWS + ROWS, a.b)) + kKeyTile - 1) / kKeyTile;
@@ -465,7 +471,7 @@ void step_bf16_kernel(StepBf16Args a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = t * kKeyTile + S::key_of(half, r, hi);
-              const bool okk = key < a.b && (a.shift < 0 || key <= qi - a.shift);
+              const bool okk = key < a.kend && qi >= a.qbeg && (a.shift < 0 || key <= qi - a.shift);
               if (!okk) sa[nt][r] = -INFINITY;
             }
           }

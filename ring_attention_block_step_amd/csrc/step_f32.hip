@@ -40,8 +40,9 @@ __global__ __launch_bounds__(64) void step_f32_kernel(StepF32Args a) {
     for (int d = 0; d < D; ++d) y[d] = 0.f;
   }
 
-  const int qend = min(row0 + 64, a.b);
-  const int nkeys = a.shift < 0 ? a.b : max(0, min(a.b, qend - a.shift));
+  // Keys of the block the workgroup's last row sees (a prefix; see BlockMask).
+  const int qlast = min(row0 + 64, a.b) - 1;
+  const int nkeys = qlast < a.qbeg ? 0 : (a.shift < 0 ? a.kend : max(0, min(a.kend, qlast + 1 - a.shift)));
 
   for (int k0 = 0; k0 < nkeys; k0 += kF32Tile) {
     for (int c = threadIdx.x; c < kF32Tile * D; c += 64) {
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(64) void step_f32_kernel(StepF32Args a) {
 #pragma unroll
     for (int r = 0; r < kF32Tile; ++r) {
       const int j = k0 + r;
-      const bool ok = j < a.b && (a.shift < 0 || j <= i - a.shift);
+      const bool ok = j < a.kend && i >= a.qbeg && (a.shift < 0 || j <= i - a.shift);
       float acc = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) acc = fmaf(qr[d], ks[r][d], acc);

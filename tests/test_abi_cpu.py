@@ -72,7 +72,9 @@ def _fwd(fn, **kw):
     (dict(Hq=3, Hkv=2), 1, "Hq"),
     (dict(Hkv=0), 1, "Hq"),
     (dict(causal=2), 1, "causal"),
-    (dict(layout=2), 1, "layout"),
+    (dict(layout=3), 1, "layout"),
+    (dict(layout=-1), 1, "layout"),
+    (dict(layout=2, N=1028), 1, "multiple of 2P"),
     (dict(d=96), 2, "d_h"),
     (dict(d=256), 2, "d_h"),
 ])
@@ -118,8 +120,11 @@ def test_shard_helpers_match_layout_definitions():
     for r in range(P):
         assert ra.shard_index(N, P, "contiguous", r).tolist() == list(range(r * b, r * b + b))
         assert ra.shard_index(N, P, "striped", r).tolist() == [j * P + r for j in range(b)]
+        c = b // 2
+        assert ra.shard_index(N, P, "zigzag", r).tolist() == \
+            list(range(r * c, r * c + c)) + list(range((2 * P - 1 - r) * c, (2 * P - r) * c))
     x = torch.arange(N * 3).view(N, 3)
-    for layout in ("contiguous", "striped"):
+    for layout in ("contiguous", "striped", "zigzag"):
         packed = ra.pack_shards(x, P, layout)
         for r in range(P):
             assert torch.equal(packed[r], x[ra.shard_index(N, P, layout, r)])

@@ -39,6 +39,13 @@ SMALL = [
     _w("b1-striped", N=8, P=8, ranks=(0, 3, 7), layout="striped", Hq=2, Hkv=1),
     _w("kscale-wide-spread", N=1024, P=4, ranks=(3,), k_scale=4.0),
     _w("uniform-v", N=768, P=4, ranks=(3,), v_dist="uniform", Hq=8, Hkv=2),
+    # zigzag: chunk size b/2 = 100 splits tiles and row blocks (ragged kend and
+    # qbeg), every rank; 128-row chunks with GQA 8/1; non-causal; b = 2; P = 1
+    _w("ragged-zigzag-causal", N=800, P=4, ranks=(0, 1, 2, 3), layout="zigzag"),
+    _w("zigzag-gqa8-p8", N=2048, P=8, ranks=(0, 3, 7), Hq=8, Hkv=1, layout="zigzag"),
+    _w("zigzag-noncausal-d64", N=1024, P=4, ranks=(1,), causal=False, layout="zigzag", d=64),
+    _w("zigzag-b2", N=16, P=8, ranks=(0, 4, 7), layout="zigzag", Hq=2, Hkv=1),
+    _w("zigzag-p1", N=334, P=1, ranks=(0,), layout="zigzag"),
 ]
 
 
@@ -54,6 +61,7 @@ F32_SMALL = [
     wl.WORKLOADS["tiny-ring-f32"],
     _w("f32-ragged-causal-gqa", N=600, P=4, ranks=(0, 3), Hq=4, Hkv=2, d=128, dtype="f32"),
     _w("f32-striped-causal", N=512, P=8, ranks=(0, 6), Hq=2, Hkv=1, d=64, dtype="f32", layout="striped"),
+    _w("f32-zigzag-causal", N=600, P=3, ranks=(0, 1, 2), Hq=4, Hkv=2, d=64, dtype="f32", layout="zigzag"),
 ]
 
 
@@ -87,6 +95,8 @@ FULL = [
     ("32k-striped-causal", 256),
     ("128k-contiguous-causal", 64),
     ("1m-contiguous-causal", 64),
+    ("32k-zigzag-causal", 256),
+    ("1m-zigzag-causal", 64),
 ]
 
 
@@ -97,7 +107,7 @@ def test_bf16_full_size_sampled_rows(name, rows):
     check(w, stats)
 
 
-@pytest.mark.parametrize("name", ["32k-contiguous-causal", "32k-striped-causal"])
+@pytest.mark.parametrize("name", ["32k-contiguous-causal", "32k-striped-causal", "32k-zigzag-causal"])
 def test_bf16_32k_every_row_of_two_heads(name):
     """Every query row of the first and the last query head (key/value heads 0
     and 7), at the full 32k shape."""
@@ -129,7 +139,7 @@ def test_equal_keys_give_mean_of_allowed_values():
     q_glob = torch.randn(N, Hq, d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
     vv = v_glob.double().numpy()[:, 0, :]
     prefix = np.cumsum(vv, axis=0) / np.arange(1, N + 1)[:, None]
-    for layout in ("contiguous", "striped"):
+    for layout in ("contiguous", "striped", "zigzag"):
         for rank in (0, 3):
             idx = ra.shard_index(N, P, layout, rank)
             q = q_glob[idx].cuda()
@@ -144,7 +154,7 @@ def test_equal_keys_give_mean_of_allowed_values():
                 assert np.abs(lse.cpu().numpy()[h] - (s0 + np.log(tq + 1))).max() <= 1e-3
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("boost", [0.35, 3.0])
 def test_late_dominant_key(layout, boost):
     """One key, late in the sequence, scores far above everything before it.

@@ -47,7 +47,7 @@ class Workload:
     N: int
     P: int
     ranks: tuple
-    layout: str          # "contiguous" | "striped"
+    layout: str          # "contiguous" | "striped" | "zigzag"
     causal: bool
     Hq: int
     Hkv: int
@@ -90,6 +90,16 @@ WORKLOADS = {
         "1m-contiguous-causal", N=1048576, P=8, ranks=(7,), layout="contiguous",
         causal=True, Hq=4, Hkv=1, d=128, dtype="bf16", seed=5, k_scale=2.0,
         note="N=1048576, P=8 contiguous, rank 7, 4/1 GQA, d=128, bf16, K x 2.0, causal"),
+    # Zigzag shards (2P chunks, shard r = chunks r and 2P-1-r): the balanced
+    # causal layout, at the 32k and million-token shapes of the workloads above.
+    "32k-zigzag-causal": Workload(
+        "32k-zigzag-causal", N=32768, P=8, ranks=(2,), layout="zigzag",
+        causal=True, Hq=32, Hkv=8, d=128, dtype="bf16", seed=6,
+        note="N=32768, P=8 zigzag (chunks r, 15-r), rank 2, 32/8 GQA, d=128, bf16, causal"),
+    "1m-zigzag-causal": Workload(
+        "1m-zigzag-causal", N=1048576, P=8, ranks=(3,), layout="zigzag",
+        causal=True, Hq=4, Hkv=1, d=128, dtype="bf16", seed=7, k_scale=2.0,
+        note="N=1048576, P=8 zigzag (chunks r, 15-r), rank 3, 4/1 GQA, d=128, bf16, K x 2.0, causal"),
 }
 
 
