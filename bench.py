@@ -64,6 +64,25 @@ def useful_pairs(layout: str, u: int, P: int, b: int, causal: bool) -> int:
     raise ValueError(layout)
 
 
+def decode_flops(n_q: int, n_keys: int, d: int, heads: int) -> float:
+    """Decode attention of n_q new tokens against n_keys cached keys: every key
+    is allowed, 4*d FLOPs per (query, key) pair and head (darshanfofadiya.com
+    4.9.4.2: heads x 4 x 1 x keys x d)."""
+    return 4.0 * d * heads * n_q * n_keys
+
+
+def decode_kv_bytes(n_keys: int, Hkv: int, d: int, elem: int = 2) -> int:
+    """Bytes of the resident key/value shard a decode step reads: K and V,
+    n_keys x Hkv x d each (darshanfofadiya.com 4.9.4.2, "KV cache reading")."""
+    return 2 * n_keys * Hkv * d * elem
+
+
+def decode_bytes(n_q: int, n_keys: int, Hq: int, Hkv: int, d: int) -> int:
+    """Algorithmic HBM bytes of one decode partial: the bf16 key/value shard
+    and query rows read, the fp32 partial (m, z, y) written."""
+    return decode_kv_bytes(n_keys, Hkv, d) + n_q * Hq * d * 2 + n_q * Hq * (d + 2) * 4
+
+
 def useful_flops(pairs: int, d: int, heads: int) -> float:
     """Two contractions per allowed pair and head, QK^T and PV: 4*d FLOPs
     (the transformer-math page's 4*b^2*d per block pair, counted on allowed

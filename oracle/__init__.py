@@ -17,7 +17,10 @@ on the pages:
   Blocks" and section 4.8.1 "Skipping Fully-Masked Blocks";
 * the transformer-math page on Ring Attention (aicassindra.com), sections "The
   mechanism, compressed", "Causal masking wastes half the ring" and "The ring is
-  a prefill algorithm" (the rescale-and-add merge of partial triples).
+  a prefill algorithm" (the rescale-and-add merge of partial triples, and the
+  decode split that keeps key/value shards stationary);
+* "Ring Attention" (darshanfofadiya.com) 4.8.3 (the zigzag assignment) and
+  4.9.4.4 (pass-Q decode).
 
 Every function is pinned by ``tests/test_oracle.py`` against values the pages
 print, closed forms, brute force on tiny inputs and invariants.  No function
@@ -28,6 +31,7 @@ from .ring_oracle import (  # noqa: F401
     NEG_INF,
     allowed_mask,
     allowed_pair_count,
+    decode_partial,
     dense_attention,
     empty_state,
     finish,

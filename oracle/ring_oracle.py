@@ -224,6 +224,37 @@ def ring_forward(q_local, u: int, k, v, P: int, layout: str, causal: bool,
 
 
 # ---------------------------------------------------------------------------
+# Decode: the query passes, the key/value shard stays.
+# ---------------------------------------------------------------------------
+
+def decode_partial(q_rows, k_shard, v_shard):
+    """Partial (m, z, y) of new query rows against one resident key/value shard.
+
+    q_rows [R, Hq, d]; k_shard, v_shard [n, Hkv, d] (the shard's cached keys
+    and values, any n >= 0).  In decode the new token comes after every cached
+    one, so every key of the shard is allowed.  The transformer-math page ("The
+    ring is a prefill algorithm") keeps the cache sharded and stationary,
+    broadcasts the query, and has each device return a partial (m, l, o) for
+    one small reduction to combine; darshanfofadiya.com 4.9.4.4 passes Q
+    around the ring for the same split.  The partial is one fold of the shard
+    into the empty state, so m, z: [Hq, R] (natural log), y: [R, Hq, d]
+    unnormalised; an empty shard gives (-inf, 0, 0).
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k_shard = np.asarray(k_shard, dtype=np.float64)
+    v_shard = np.asarray(v_shard, dtype=np.float64)
+    R, Hq, d = q_rows.shape
+    n, Hkv, _ = k_shard.shape
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    m, z, y = empty_state(R, Hq, d)
+    for h in range(Hq):
+        s = (q_rows[:, h, :] @ k_shard[:, h // G, :].T) * scale
+        m[h], z[h], y[:, h, :] = online_fold(m[h], z[h], y[:, h, :], s, v_shard[:, h // G, :])
+    return m, z, y
+
+
+# ---------------------------------------------------------------------------
 # Merge of partial (m, z, y) triples.
 # ---------------------------------------------------------------------------
 

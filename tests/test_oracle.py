@@ -464,6 +464,77 @@ def test_merge_of_block_partials_equals_dense(layout):
     np.testing.assert_allclose(lse, lse_d, rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# Decode: partial triples of resident shards.
+# ---------------------------------------------------------------------------
+
+def test_decode_partial_single_shard_is_softmax():
+    """One shard: y / z is scipy's softmax of the scaled scores times V,
+    m is the largest scaled score and LSE = m + ln z = logsumexp."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(41)
+    R, Hq, Hkv, d, n = 3, 4, 2, 16, 37
+    q = rng.standard_normal((R, Hq, d))
+    k = rng.standard_normal((n, Hkv, d)) * 2
+    v = rng.standard_normal((n, Hkv, d))
+    m, z, y = ro.decode_partial(q, k, v)
+    for h in range(Hq):
+        s = q[:, h, :] @ k[:, h // 2, :].T / np.sqrt(d)
+        np.testing.assert_allclose(y[:, h, :] / z[h][:, None], scipy_softmax(s, axis=1) @ v[:, h // 2, :],
+                                   rtol=0, atol=1e-12)
+        np.testing.assert_allclose(m[h], s.max(axis=1), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(m[h] + np.log(z[h]), logsumexp(s, axis=1), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("sizes", [(8, 8, 8, 8), (5, 0, 11, 1, 7), (0, 0, 3)])
+def test_decode_partials_merge_to_dense(sizes):
+    """Pass-Q decode: each shard's partial against the broadcast query,
+    merged, equals dense attention of the new tokens over the whole cache
+    (every cached key precedes them); empty shards are neutral."""
+    rng = np.random.default_rng(sum(sizes))
+    N = sum(sizes)
+    n_q, Hq, Hkv, d = 2, 4, 2, 8
+    q = rng.standard_normal((n_q, Hq, d))
+    k = rng.standard_normal((N, Hkv, d)) * 1.5
+    v = rng.standard_normal((N, Hkv, d))
+    parts = []
+    lo = 0
+    for n in sizes:
+        parts.append(ro.decode_partial(q, k[lo:lo + n], v[lo:lo + n]))
+        lo += n
+    m = np.stack([p[0] for p in parts])
+    z = np.stack([p[1] for p in parts])
+    y = np.stack([np.transpose(p[2], (1, 0, 2)) for p in parts])   # [n, Hq, R, d]
+    o, lse = ro.merge_partials(m, z, y)
+    o_d, lse_d = ro.dense_attention(q, np.full(n_q, N), k, v, causal=True)
+    np.testing.assert_allclose(np.transpose(o, (1, 0, 2)), o_d, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_d, rtol=0, atol=1e-12)
+
+
+def test_decode_partial_of_empty_shard_is_merge_identity():
+    m, z, y = ro.decode_partial(np.ones((2, 2, 4)), np.zeros((0, 1, 4)), np.zeros((0, 1, 4)))
+    assert np.all(m == -np.inf) and np.all(z == 0) and np.all(y == 0)
+
+
+def test_decode_budget_figures():
+    """Decode accounting reproduces the per-GPU figures printed for 1M context
+    on 32 GPUs: 128 MB of K and V, 1.02e9 attention FLOPs, a 16 KB query."""
+    import bench
+    g = _load("decode_budget.json")
+    tol = g["printed_rel_precision"]
+    kv = bench.decode_kv_bytes(g["local_tokens"], g["kv_heads"], g["d_h"], g["bytes_per_elem"])
+    assert abs(kv / g["printed_kv_bytes"] - 1) <= tol
+    assert abs(kv / 2e12 * 1e3 / g["printed_kv_read_ms_at_2TBps"] - 1) <= tol
+    fl = bench.decode_flops(g["new_tokens"], g["local_tokens"], g["d_h"], g["query_heads"])
+    assert abs(fl / g["printed_attention_flops"] - 1) <= tol
+    assert abs(fl / 175e12 * 1e3 / g["printed_attention_ms_at_175TFLOPs"] - 1) <= 0.1   # printed to 1 digit
+    q_bytes = g["new_tokens"] * g["query_heads"] * g["d_h"] * g["bytes_per_elem"]
+    assert q_bytes == g["printed_q_bytes_one_token"]
+    # the decode partial's byte count is the shard plus the query and the fp32 triple
+    full = bench.decode_bytes(1, g["local_tokens"], g["query_heads"], g["kv_heads"], g["d_h"])
+    assert full == kv + q_bytes + g["query_heads"] * (g["d_h"] + 2) * 4
+
+
 def test_merge_identity_associativity_commutativity():
     rng = np.random.default_rng(22)
     n, R, d = 5, 7, 4
@@ -579,7 +650,8 @@ def _pins_fail():
                lambda: test_all_equal_keys_give_mean_of_allowed_values("contiguous", True),
                lambda: test_ring_equals_dense(*RING_CASES[3]),
                lambda: test_brute_force_tiny("zigzag", True, 4),
-               test_zigzag_balance_matches_page]
+               test_zigzag_balance_matches_page,
+               test_decode_partial_single_shard_is_softmax]
     for c in checks:
         try:
             with np.errstate(all="ignore"):
@@ -635,6 +707,20 @@ def test_planted_gqa_mistake_is_caught(monkeypatch):
     assert _pins_fail()
 
 
+def test_planted_decode_mistake_is_caught(monkeypatch):
+    real = ro.decode_partial
+
+    def no_rescale_of_v(q, k, v):
+        m, z, y = real(q, k, v)
+        return m, z, y * 1.01          # y off by a constant factor
+    monkeypatch.setattr(ro, "decode_partial", no_rescale_of_v)
+    with pytest.raises(AssertionError):
+        test_decode_partial_single_shard_is_softmax()
+    with pytest.raises(AssertionError):
+        test_decode_partials_merge_to_dense((5, 0, 11, 1, 7))
+
+
 def test_package_exports():
+    assert oracle.decode_partial is ro.decode_partial
     assert oracle.ring_forward is ro.ring_forward
     assert oracle.merge_partials is ro.merge_partials
