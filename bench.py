@@ -13,9 +13,13 @@ step.  ``roofline`` reports the step kernel against the MI355X bf16 dense MFMA
 peak, with its average launch duration measured by HIP events around every step
 kernel inside the timed region.  ``cpu_baseline`` times the fp64 oracle on the
 host cores on a bounded sample of query rows of the same workload.
+``merge_kernel`` and ``decode_kernel`` report the two HBM-bound kernels (the
+triple merge; the pass-Q decode partial of one resident shard) as achieved GB/s
+against 8 TB/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--cpu-seconds S] [--no-cpu-baseline]
+                       [--cpu-seconds S] [--no-cpu-baseline] [--no-merge]
+                       [--no-decode] [--decode-workload NAME] [--decode-only]
 """
 
 from __future__ import annotations
@@ -217,6 +221,40 @@ def measure_merge(reps: int = 10) -> dict:
             "frac": gbs / PEAK_HBM_GBS, "launches": t["merge_launches"]}
 
 
+def measure_decode(name: str = "decode-31k-gqa64", reps: int = 20) -> dict:
+    """Time ringattn_decode_partial on one resident shard of a decode workload
+    (HIP events around the call's kernels, inside the library) and report the
+    achieved GB/s of its algorithmic bytes against 8 TB/s."""
+    import torch
+
+    import ring_attention_block_step_amd as ra
+    import workloads as wl
+
+    w = wl.DECODE_WORKLOADS[name]
+    q = wl.decode_query(w).cuda()
+    k, v = (t.cuda() for t in wl.decode_shard(w, w.P - 1))
+    m = torch.empty(w.Hq, w.n_q, device="cuda")
+    z = torch.empty_like(m)
+    y = torch.empty(w.n_q, w.Hq, w.d, device="cuda")
+    for _ in range(3):
+        ra.decode_partial(q, k, v, m=m, z=z, y=y)
+    torch.cuda.synchronize()
+    ra.timing_collect_decode()
+    ra.timing_enable(True)
+    for _ in range(reps):
+        ra.decode_partial(q, k, v, m=m, z=z, y=y)
+    torch.cuda.synchronize()
+    ra.timing_enable(False)
+    t = ra.timing_collect_decode()
+    avg_ms = t["decode_ms"] / max(1, t["decode_calls"])
+    nbytes = decode_bytes(w.n_q, w.n_keys, w.Hq, w.Hkv, w.d)
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    return {"kernel": "decode_chunk_kernel<128>+decode_combine_kernel<128>", "workload": name,
+            "shape": {"n_q": w.n_q, "n_keys": w.n_keys, "Hq": w.Hq, "Hkv": w.Hkv, "d_h": w.d},
+            "bytes_per_call": nbytes, "avg_call_ms": avg_ms, "achieved": gbs, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "calls": t["decode_calls"]}
+
+
 def copy_calibration(nbytes: int, reps: int = 3) -> None:
     """A plain device copy of known size (torch's copy kernel), for scaling the
     FETCH_SIZE / WRITE_SIZE counters of other kernels."""
@@ -243,6 +281,11 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true", help="skip the merge-kernel measurement")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-kernel measurement")
+    ap.add_argument("--decode-workload", default="decode-31k-gqa64",
+                    help="decode workload of the decode-kernel measurement")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only run the decode-kernel measurement and print its JSON object")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -262,6 +305,9 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         return 3
+    if args.decode_only:
+        print(json.dumps(measure_decode(args.decode_workload)), flush=True)
+        return 0
     if args.copy_bytes:
         copy_calibration(args.copy_bytes)
         return 0
@@ -327,6 +373,7 @@ def main(argv=None) -> int:
     }
 
     merge = None if args.no_merge else measure_merge()
+    decode = None if args.no_decode else measure_decode(args.decode_workload)
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
@@ -353,6 +400,7 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "merge_kernel": merge,
+        "decode_kernel": decode,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -105,6 +105,37 @@ int ringattn_merge(const float* m, const float* z, const float* y, int nparts,
                    int64_t rows, int Hq, int d_h, void* out, int out_dtype,
                    float* lse, void* stream);
 
+/*
+ * ringattn_decode_partial -- pass-Q decode on one device: the new query rows
+ * meet the device's resident key/value shard, which stays in place, and give
+ * a partial (m, z, y) triple; ringattn_merge combines the P devices' partials
+ * into O and LSE (the transformer-math page (aicassindra.com), "The ring is a
+ * prefill algorithm": keep the cache sharded and stationary, broadcast the
+ * query, combine P partial (m, l, o) with one small reduction; "Ring
+ * Attention" (darshanfofadiya.com) 4.9.4.4, the pass-Q variant).  The new
+ * tokens follow every cached key, so no key of the shard is masked:
+ *   m = max_j S_j,  z = sum_j e^{S_j - m},  y = sum_j e^{S_j - m} v_j,
+ *   S_j = q . k_j / sqrt(d_h), over the shard's n_keys keys.
+ *
+ *  q        [n_q, Hq, d_h]      bf16, the new tokens' query rows (read only)
+ *  k, v     [n_keys, Hkv, d_h]  bf16, the resident shard (read only); may be
+ *                               NULL when n_keys == 0
+ *  m, z     [Hq, n_q]           fp32 (written): m in natural-log units
+ *  y        [n_q, Hq, d_h]      fp32, unnormalised (written)
+ *  n_q >= 1, n_keys >= 0, Hq % Hkv == 0, d_h in {64, 128}.  q, k, v and y
+ *  must be 16-byte aligned, m and z 4-byte aligned.
+ *
+ * These are exactly one part of ringattn_merge's inputs: pointing m, z, y at
+ * part p of arrays [P, Hq, n_q] and [P, n_q, Hq, d_h] and then calling
+ * ringattn_merge(..., nparts = P, rows = n_q, ...) gives attention of the new
+ * tokens over every shard.  An empty shard (n_keys = 0) gives m = -inf, z = 0,
+ * y = 0, which the merge ignores.  The library takes a workspace of
+ * ceil(n_keys / 256) * Hq * n_q * (d_h + 2) floats stream-ordered on `stream`.
+ */
+int ringattn_decode_partial(const void* q, const void* k, const void* v, int n_q,
+                            int64_t n_keys, int Hq, int Hkv, int d_h,
+                            float* m, float* z, float* y, void* stream);
+
 /* Static string for a status code. */
 const char* ringattn_status_string(int status);
 
@@ -113,15 +144,21 @@ const char* ringattn_last_error(void);
 
 /*
  * Kernel timing for measurement.  While enabled (enable = 1) every step kernel
- * that ringattn_forward / ringattn_forward_f32 launches, and every merge
- * kernel, is bracketed by a pair of HIP events on the stream it runs on.
- * ringattn_timing_collect() waits for the recorded events, returns the summed
- * duration (ms) and count of the step kernels and of the merge kernels since
- * the last collect, and releases the events.  Returns a status code.
+ * that ringattn_forward / ringattn_forward_f32 launches, every merge kernel and
+ * the kernels of every ringattn_decode_partial call are bracketed by a pair of
+ * HIP events on the stream they run on.  ringattn_timing_collect() waits for
+ * the recorded step and merge events, returns the summed duration (ms) and
+ * count of the step kernels and of the merge kernels since the last collect,
+ * and releases those events.  Returns a status code.
  */
 int ringattn_timing_enable(int enable);
 int ringattn_timing_collect(double* step_ms, int64_t* step_launches,
                             double* merge_ms, int64_t* merge_launches);
+
+/* Same for ringattn_decode_partial calls: summed duration (ms) of the decode
+ * kernels of each call (chunk and combine kernels together) and the number of
+ * calls since the last collect of decode timings. */
+int ringattn_timing_collect_decode(double* decode_ms, int64_t* decode_calls);
 
 /*
  * Debug switch: when serial = 1 every key/value hop copy runs on the caller's

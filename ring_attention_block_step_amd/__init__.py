@@ -7,7 +7,8 @@ computation runs in the library's HIP kernels; there is no CPU or PyTorch
 fallback, and using any entry point without the built library raises.
 
 Names follow the C ABI: ``forward`` (``ringattn_forward`` for bf16,
-``ringattn_forward_f32`` for fp32), ``merge`` (``ringattn_merge``).
+``ringattn_forward_f32`` for fp32), ``merge`` (``ringattn_merge``),
+``decode_partial`` (``ringattn_decode_partial``).
 """
 
 from __future__ import annotations
@@ -17,16 +18,17 @@ import os
 
 import torch
 
-__all__ = ["forward", "merge", "shard_index", "pack_shards", "lib", "RingAttnError",
-           "timing_enable", "timing_collect", "set_serial_hops", "version", "SYMBOLS", "LIB_PATH"]
+__all__ = ["forward", "merge", "decode_partial", "shard_index", "pack_shards", "lib", "RingAttnError",
+           "timing_enable", "timing_collect", "timing_collect_decode", "set_serial_hops", "version", "SYMBOLS",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
 LAYOUTS = {"contiguous": 0, "striped": 1, "zigzag": 2}
 
 # Every symbol include/ringattn.h declares.
-SYMBOLS = ("ringattn_forward", "ringattn_forward_f32", "ringattn_merge", "ringattn_status_string",
-           "ringattn_last_error", "ringattn_timing_enable", "ringattn_timing_collect",
-           "ringattn_set_serial_hops", "ringattn_version")
+SYMBOLS = ("ringattn_forward", "ringattn_forward_f32", "ringattn_merge", "ringattn_decode_partial",
+           "ringattn_status_string", "ringattn_last_error", "ringattn_timing_enable", "ringattn_timing_collect",
+           "ringattn_timing_collect_decode", "ringattn_set_serial_hops", "ringattn_version")
 
 _lib = None
 
@@ -53,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.ringattn_forward_f32.restype = i32
     L.ringattn_merge.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, i32, f32p, vp]
     L.ringattn_merge.restype = i32
+    L.ringattn_decode_partial.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp]
+    L.ringattn_decode_partial.restype = i32
     L.ringattn_status_string.argtypes = [i32]
     L.ringattn_status_string.restype = ctypes.c_char_p
     L.ringattn_last_error.argtypes = []
@@ -62,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.ringattn_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.ringattn_timing_collect.restype = i32
+    L.ringattn_timing_collect_decode.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.ringattn_timing_collect_decode.restype = i32
     L.ringattn_set_serial_hops.argtypes = [i32]
     L.ringattn_set_serial_hops.restype = i32
     L.ringattn_version.argtypes = []
@@ -198,6 +204,39 @@ def merge(m: torch.Tensor, z: torch.Tensor, y: torch.Tensor, *, out_dtype=torch.
     return out, lse
 
 
+def decode_partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, m: torch.Tensor | None = None,
+                   z: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """Partial (m, z, y) of new query rows q [n_q, Hq, d] against a resident
+    shard k, v [n_keys, Hkv, d], all bf16 on one device (n_keys may be 0).
+
+    Returns m, z [Hq, n_q] (natural log) and y [n_q, Hq, d], fp32; pass views
+    of part p of merge's inputs ([P, Hq, n_q], [P, n_q, Hq, d]) to fill them
+    in place.  Asynchronous on the current stream of q's device.
+    """
+    L = lib()
+    _need(q.is_cuda and k.is_cuda and v.is_cuda and q.device == k.device == v.device,
+          "q, k, v must be device tensors on one device")
+    _need(q.dtype == k.dtype == v.dtype == torch.bfloat16, "q, k, v must be bfloat16")
+    _need(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "q, k, v must be contiguous")
+    _need(q.dim() == 3 and k.dim() == 3 and v.shape == k.shape, "q [n_q, Hq, d], k and v [n_keys, Hkv, d]")
+    n_q, Hq, d = q.shape
+    n_keys, Hkv = k.shape[0], k.shape[1]
+    _need(k.shape[2] == d, "k, v must have q's d")
+    if m is None:
+        m = torch.empty((Hq, n_q), dtype=torch.float32, device=q.device)
+    if z is None:
+        z = torch.empty((Hq, n_q), dtype=torch.float32, device=q.device)
+    if y is None:
+        y = torch.empty((n_q, Hq, d), dtype=torch.float32, device=q.device)
+    for t, shape, name in ((m, (Hq, n_q), "m"), (z, (Hq, n_q), "z"), (y, (n_q, Hq, d), "y")):
+        _need(tuple(t.shape) == shape and t.dtype == torch.float32 and t.is_contiguous() and t.device == q.device,
+              f"{name} must be float32 {list(shape)} on q's device")
+    with torch.cuda.device(q.device):
+        _check(L.ringattn_decode_partial(_ptr(q), _ptr(k) if n_keys else None, _ptr(v) if n_keys else None,
+                                         n_q, n_keys, Hq, Hkv, d, _ptr(m), _ptr(z), _ptr(y), _stream(q.device)))
+    return m, z, y
+
+
 def timing_enable(flag: bool = True) -> None:
     _check(lib().ringattn_timing_enable(int(bool(flag))))
 
@@ -208,6 +247,13 @@ def timing_collect() -> dict:
     sn, mn = ctypes.c_int64(), ctypes.c_int64()
     _check(lib().ringattn_timing_collect(ctypes.byref(sm), ctypes.byref(sn), ctypes.byref(mm), ctypes.byref(mn)))
     return {"step_ms": sm.value, "step_launches": sn.value, "merge_ms": mm.value, "merge_launches": mn.value}
+
+
+def timing_collect_decode() -> dict:
+    """Summed decode kernel durations (ms) and call count since the last collect."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib().ringattn_timing_collect_decode(ctypes.byref(ms), ctypes.byref(n)))
+    return {"decode_ms": ms.value, "decode_calls": n.value}
 
 
 def set_serial_hops(flag: bool) -> None:

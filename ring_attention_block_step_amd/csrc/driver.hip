@@ -65,7 +65,7 @@ DeviceCtx g_dev[kMaxDevices];
 
 struct TimedLaunch {
   hipEvent_t begin, end;
-  int kind;  // 0 step, 1 merge
+  int kind;  // 0 step, 1 merge, 2 decode
 };
 std::mutex g_timing_mu;
 bool g_timing = false;
@@ -240,6 +240,32 @@ int run_ring(int P, int rank, int b, int causal, int layout, size_t slot_bytes, 
   return status;
 }
 
+// Waits for and releases the recorded launches whose kind is in `kinds` (bit
+// mask), adding their durations (ms) and counts per kind; others stay queued.
+int collect_timing(int kinds, double* sums, int64_t* counts) {
+  std::vector<TimedLaunch> taken;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    std::vector<TimedLaunch> keep;
+    for (auto& t : g_timed) ((kinds >> t.kind) & 1 ? taken : keep).push_back(t);
+    g_timed.swap(keep);
+  }
+  int status = RINGATTN_OK;
+  for (auto& t : taken) {
+    float ms = 0.f;
+    if (status == RINGATTN_OK) {
+      hipError_t e = hipEventSynchronize(t.end);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.begin, t.end);
+      if (e != hipSuccess) status = fail(RINGATTN_EHIP, "timing events: %s", hipGetErrorString(e));
+    }
+    sums[t.kind] += ms;
+    counts[t.kind] += 1;
+    (void)hipEventDestroy(t.begin);
+    (void)hipEventDestroy(t.end);
+  }
+  return status;
+}
+
 }  // namespace
 
 extern "C" {
@@ -379,6 +405,57 @@ int ringattn_merge(const float* m, const float* z, const float* y, int nparts, i
   return RINGATTN_OK;
 }
 
+int ringattn_decode_partial(const void* q, const void* k, const void* v, int n_q, int64_t n_keys, int Hq, int Hkv,
+                            int d_h, float* m, float* z, float* y, void* stream) {
+  if (!q || !m || !z || !y) return fail(RINGATTN_EINVAL, "q, m, z and y must be non-null");
+  if (n_keys > 0 && (!k || !v)) return fail(RINGATTN_EINVAL, "k and v must be non-null when n_keys > 0");
+  if (!aligned16(q) || (n_keys > 0 && (!aligned16(k) || !aligned16(v))))
+    return fail(RINGATTN_EINVAL, "q, k and v must be 16-byte aligned");
+  if (!aligned16(y) || ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(z)) & 3))
+    return fail(RINGATTN_EINVAL, "y must be 16-byte aligned, m and z 4-byte aligned");
+  if (n_q < 1) return fail(RINGATTN_EINVAL, "n_q must be >= 1 (got %d)", n_q);
+  if (n_keys < 0) return fail(RINGATTN_EINVAL, "n_keys must be >= 0");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(RINGATTN_EINVAL, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (got %d, %d)", Hq, Hkv);
+  if (d_h != 64 && d_h != 128) return fail(RINGATTN_EUNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
+  const int64_t rows = (int64_t)(Hq / Hkv) * n_q;
+  const int64_t nchunks = (n_keys + kDecodeChunk - 1) / kDecodeChunk;
+  if (rows * Hkv > ((int64_t)1 << 30) || nchunks > ((int64_t)1 << 30) || (rows + 15) / 16 > 65535)
+    return fail(RINGATTN_EUNSUPPORTED, "decode shape too large (n_q=%d, Hq=%d, n_keys=%lld)", n_q, Hq,
+                (long long)n_keys);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DecodeArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.m_out = m;
+  a.z_out = z;
+  a.y_out = y;
+  a.n_keys = n_keys;
+  a.n_q = n_q;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.rows = (int)rows;
+  a.nchunks = (int)nchunks;
+  a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)d_h));
+  const size_t parts = (size_t)nchunks * Hkv * rows;
+  const size_t mz_bytes = round_up(parts * sizeof(float), 256);
+  const size_t ws_bytes = 2 * mz_bytes + parts * d_h * sizeof(float);
+  void* ws = nullptr;
+  if (ws_bytes > 0) HIP_TRY(hipMallocAsync(&ws, ws_bytes, st));
+  a.ws_m = static_cast<float*>(ws);
+  a.ws_z = reinterpret_cast<float*>(static_cast<char*>(ws) + mz_bytes);
+  a.ws_y = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * mz_bytes);
+  const int tix = timing_begin(st, 2);
+  hipError_t e = launch_decode(a, d_h, st);
+  timing_end(tix, st);
+  hipError_t fe = ws ? hipFreeAsync(ws, st) : hipSuccess;
+  if (e != hipSuccess) return fail(RINGATTN_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+  if (fe != hipSuccess) return fail(RINGATTN_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+  return RINGATTN_OK;
+}
+
 const char* ringattn_status_string(int status) {
   switch (status) {
     case RINGATTN_OK: return "ok";
@@ -398,30 +475,22 @@ int ringattn_timing_enable(int enable) {
 }
 
 int ringattn_timing_collect(double* step_ms, int64_t* step_launches, double* merge_ms, int64_t* merge_launches) {
-  std::vector<TimedLaunch> taken;
-  {
-    std::lock_guard<std::mutex> lk(g_timing_mu);
-    taken.swap(g_timed);
-  }
-  double sums[2] = {0.0, 0.0};
-  int64_t counts[2] = {0, 0};
-  int status = RINGATTN_OK;
-  for (auto& t : taken) {
-    float ms = 0.f;
-    if (status == RINGATTN_OK) {
-      hipError_t e = hipEventSynchronize(t.end);
-      if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.begin, t.end);
-      if (e != hipSuccess) status = fail(RINGATTN_EHIP, "timing events: %s", hipGetErrorString(e));
-    }
-    sums[t.kind] += ms;
-    counts[t.kind] += 1;
-    (void)hipEventDestroy(t.begin);
-    (void)hipEventDestroy(t.end);
-  }
+  double sums[3] = {0.0, 0.0, 0.0};
+  int64_t counts[3] = {0, 0, 0};
+  const int status = collect_timing(0x3, sums, counts);
   if (step_ms) *step_ms = sums[0];
   if (step_launches) *step_launches = counts[0];
   if (merge_ms) *merge_ms = sums[1];
   if (merge_launches) *merge_launches = counts[1];
+  return status;
+}
+
+int ringattn_timing_collect_decode(double* decode_ms, int64_t* decode_calls) {
+  double sums[3] = {0.0, 0.0, 0.0};
+  int64_t counts[3] = {0, 0, 0};
+  const int status = collect_timing(0x4, sums, counts);
+  if (decode_ms) *decode_ms = sums[2];
+  if (decode_calls) *decode_calls = counts[2];
   return status;
 }
 

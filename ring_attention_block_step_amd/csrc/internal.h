@@ -74,6 +74,26 @@ struct StepF32Args {
   float scale;       // 1 / sqrt(D)
 };
 
+// Pass-Q decode: keys per workgroup of the chunk kernel.
+constexpr int kDecodeChunk = 256;
+
+struct DecodeArgs {
+  const __bf16* q;   // [n_q, Hq, D] new query rows
+  const __bf16* k;   // [n_keys, Hkv, D] resident shard
+  const __bf16* v;
+  float* ws_m;       // [nchunks][Hkv][rows] chunk maxima (log2 units)
+  float* ws_z;       // [nchunks][Hkv][rows]
+  float* ws_y;       // [nchunks][Hkv][rows][D]
+  float* m_out;      // [Hq, n_q] natural-log units
+  float* z_out;      // [Hq, n_q]
+  float* y_out;      // [n_q, Hq, D]
+  int64_t n_keys;
+  int n_q, Hq, Hkv, G;
+  int rows;          // G * n_q query rows per key/value head (row = token * G + head in group)
+  int nchunks;       // ceil(n_keys / kDecodeChunk)
+  float sl2;         // log2(e) / sqrt(D)
+};
+
 // Byte offset of 16-byte chunk `chunk` of row `row` inside one 64-key tile of a
 // slot, which is also its LDS image (tiles are copied to LDS verbatim).
 //  key tile:   64 rows (keys) x D bf16, chunk c = d 8c .. 8c+7;
@@ -105,5 +125,8 @@ int step_bf16_grid(const StepBf16Args& a);
 hipError_t launch_step_f32(const StepF32Args& a, int D, hipStream_t st);
 hipError_t launch_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows,
                         int Hq, int D, void* out, int out_f32, float* lse, hipStream_t st);
+// Chunk kernel (skipped when nchunks == 0), then the combine kernel.
+hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t st);
+int decode_row_block(int rows);
 
 }  // namespace ringattn

@@ -99,6 +99,24 @@ def test_merge_rejects_bad_arguments_and_accepts_empty():
     assert m(FAKE, FAKE, FAKE, 2, 0, 4, 128, FAKE, 0, None, None) == 0
 
 
+def test_decode_rejects_bad_arguments():
+    L = _lib()
+    d = L.ringattn_decode_partial
+    # q, k, v, n_q, n_keys, Hq, Hkv, d_h, m, z, y, stream
+    assert d(None, FAKE, FAKE, 1, 10, 4, 1, 128, FAKE, FAKE, FAKE, None) == 1
+    assert d(FAKE, None, FAKE, 1, 10, 4, 1, 128, FAKE, FAKE, FAKE, None) == 1
+    assert d(FAKE, FAKE, FAKE, 1, 10, 4, 1, 128, None, FAKE, FAKE, None) == 1
+    assert d(MISALIGNED, FAKE, FAKE, 1, 10, 4, 1, 128, FAKE, FAKE, FAKE, None) == 1
+    assert d(FAKE, FAKE, FAKE, 1, 10, 4, 1, 128, ctypes.c_void_p(0x10002), FAKE, FAKE, None) == 1
+    assert d(FAKE, FAKE, FAKE, 1, 10, 4, 1, 128, FAKE, FAKE, MISALIGNED, None) == 1
+    assert d(FAKE, FAKE, FAKE, 0, 10, 4, 1, 128, FAKE, FAKE, FAKE, None) == 1
+    assert d(FAKE, FAKE, FAKE, 1, -1, 4, 1, 128, FAKE, FAKE, FAKE, None) == 1
+    assert d(FAKE, FAKE, FAKE, 1, 10, 6, 4, 128, FAKE, FAKE, FAKE, None) == 1
+    assert "Hq" in L.ringattn_last_error().decode()
+    assert d(FAKE, FAKE, FAKE, 1, 10, 4, 1, 96, FAKE, FAKE, FAKE, None) == 2
+    assert "d_h" in L.ringattn_last_error().decode()
+
+
 def test_timing_collect_empty():
     _lib()
     ra.timing_enable(False)

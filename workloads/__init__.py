@@ -103,6 +103,53 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Pass-Q decode: n_q new tokens (global positions N .. N+n_q-1) against a
+    cache of N = P * n_keys tokens held as P resident shards of n_keys tokens
+    (shard p holds tokens p*n_keys .. p*n_keys + n_keys - 1); bf16."""
+
+    name: str
+    P: int
+    n_keys: int
+    n_q: int
+    Hq: int
+    Hkv: int
+    d: int
+    seed: int
+    k_scale: float = 1.0
+    note: str = field(default="", compare=False)
+
+    @property
+    def N(self) -> int:
+        return self.P * self.n_keys
+
+
+DECODE_WORKLOADS = {
+    # Per GPU of 32 at 1M context with Llama-70B's heads (64 query, 8 key/value).
+    "decode-31k-gqa64": DecodeWorkload(
+        "decode-31k-gqa64", P=32, n_keys=31250, n_q=1, Hq=64, Hkv=8, d=128, seed=8,
+        note="1 new token, 32 shards of 31,250 cached tokens, 64/8 GQA, d=128, bf16"),
+    # The million-token share's shape: 8 shards of 131,072 tokens, 4/1 GQA, K x 2.
+    "decode-1m-shard": DecodeWorkload(
+        "decode-1m-shard", P=8, n_keys=131072, n_q=1, Hq=4, Hkv=1, d=128, seed=9, k_scale=2.0,
+        note="1 new token, 8 shards of 131,072 cached tokens, 4/1 GQA, d=128, bf16, K x 2.0"),
+}
+
+
+def decode_query(w: DecodeWorkload) -> torch.Tensor:
+    """The new tokens' query rows, [n_q, Hq, d] bf16."""
+    return token_range(w.seed, "q", w.N, w.N + w.n_q, w.Hq, w.d, "normal", 1.0, torch.bfloat16)
+
+
+def decode_shard(w: DecodeWorkload, p: int):
+    """Cached K and V of shard p, [n_keys, Hkv, d] bf16 each."""
+    lo, hi = p * w.n_keys, (p + 1) * w.n_keys
+    k = token_range(w.seed, "k", lo, hi, w.Hkv, w.d, "normal", w.k_scale, torch.bfloat16)
+    v = token_range(w.seed, "v", lo, hi, w.Hkv, w.d, "normal", 1.0, torch.bfloat16)
+    return k, v
+
+
 def _draw(gen: torch.Generator, shape, dist: str) -> torch.Tensor:
     if dist == "normal":
         return torch.randn(shape, generator=gen, dtype=torch.float32)
