@@ -18,7 +18,9 @@ on the pages:
 * the transformer-math page on Ring Attention (aicassindra.com), sections "The
   mechanism, compressed", "Causal masking wastes half the ring" and "The ring is
   a prefill algorithm" (the rescale-and-add merge of partial triples, and the
-  decode split that keeps key/value shards stationary);
+  decode split that keeps key/value shards stationary) and "The backward pass
+  costs a second ring" (the backward ring with scores rebuilt from the saved
+  statistics);
 * "Ring Attention" (darshanfofadiya.com) 4.8.3 (the zigzag assignment) and
   4.9.4.4 (pass-Q decode).
 
@@ -31,12 +33,14 @@ from .ring_oracle import (  # noqa: F401
     NEG_INF,
     allowed_mask,
     allowed_pair_count,
+    backward_dense,
     decode_partial,
     dense_attention,
     empty_state,
     finish,
     merge_partials,
     online_fold,
+    ring_backward,
     ring_forward,
     shard_positions,
 )

@@ -224,6 +224,101 @@ def ring_forward(q_local, u: int, k, v, P: int, layout: str, causal: bool,
 
 
 # ---------------------------------------------------------------------------
+# Backward: gradients of L = sum(dO * O).
+# ---------------------------------------------------------------------------
+
+def backward_dense(q_rows, tq, k, v, dout, causal: bool):
+    """Gradients of L = sum_{i,h,c} dO[i,h,c] O[i,h,c] for O = dense attention.
+
+    The softmax Jacobian written out, per query head h (KV head h // G), with
+    P the masked softmax of S = Q K^T / sqrt(d) and O = P V:
+      dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(dP * P)),
+      dQ = dS K / sqrt(d),   dK = dS^T Q / sqrt(d).
+    Query heads of one group add into their key/value head's dK, dV.  Returns
+    dq [R, Hq, d] and dk, dv [N, Hkv, d] over the whole sequence.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    R, Hq, d = q_rows.shape
+    N, Hkv, _ = k.shape
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    allow = allowed_mask(tq, np.arange(N), causal)
+    has = allow.any(axis=1)
+    dq = np.zeros((R, Hq, d))
+    dk = np.zeros((N, Hkv, d))
+    dv = np.zeros((N, Hkv, d))
+    for h in range(Hq):
+        kh, vh = k[:, h // G, :], v[:, h // G, :]
+        s = np.where(allow, (q_rows[:, h, :] @ kh.T) * scale, NEG_INF)
+        mx = np.where(has, s.max(axis=1), 0.0)
+        e = np.where(allow, np.exp(s - mx[:, None]), 0.0)
+        p = e / np.where(has, e.sum(axis=1), 1.0)[:, None]
+        do = dout[:, h, :]
+        dv[:, h // G, :] += p.T @ do
+        dp = do @ vh.T
+        ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+        dq[:, h, :] = ds @ kh * scale
+        dk[:, h // G, :] += ds.T @ q_rows[:, h, :] * scale
+    return dq, dk, dv
+
+
+def ring_backward(q_local, u: int, k, v, out, lse, dout, P: int, layout: str, causal: bool, order=None):
+    """Rank u's share of the backward ring.
+
+    The transformer-math page ("The backward pass costs a second ring"): the
+    key/value blocks rotate again with their gradient accumulators, every
+    device adds its contribution as a block passes, and the [b, b] scores are
+    rebuilt from the saved row statistics and output instead of being stored.
+    For each visiting block r (order as in ring_forward):
+      S = Q K_r^T / sqrt(d) (masked),  P = e^{S - LSE}  (LSE saved by the
+      forward, natural log),  D = rowsum(dO * O)  (O saved by the forward),
+      dV_r += P^T dO,  dP = dO V_r^T,  dS = P * (dP - D),
+      dQ += dS K_r / sqrt(d),  dK_r += dS^T Q / sqrt(d).
+    q_local, out, dout [b, Hq, d]; lse [Hq, b]; k, v global [N, Hkv, d].
+    Returns dq [b, Hq, d] and rank u's contributions dk, dv [P, b, Hkv, d] to
+    every shard (local row order; zero for blocks it never sees).  A row with
+    LSE = -inf saw no key and contributes nothing.
+    """
+    q_local = np.asarray(q_local, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    b, Hq, d = q_local.shape
+    N, Hkv, _ = k.shape
+    if N != P * b:
+        raise ValueError("the sequence must split into P shards of b tokens")
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    tq = shard_positions(layout, u, P, b)
+    live = np.isfinite(lse)                                   # [Hq, b]
+    lse_safe = np.where(live, lse, 0.0)
+    D = (dout * out).sum(axis=2).T                            # [Hq, b]
+    dq = np.zeros((b, Hq, d))
+    dk = np.zeros((P, b, Hkv, d))
+    dv = np.zeros((P, b, Hkv, d))
+    visits = [(u - s) % P for s in range(P)] if order is None else list(order)
+    for r in visits:
+        tk = shard_positions(layout, r, P, b)
+        allow = allowed_mask(tq, tk, causal)
+        for h in range(Hq):
+            kr, vr = k[tk, h // G, :], v[tk, h // G, :]
+            s = (q_local[:, h, :] @ kr.T) * scale
+            p = np.where(allow & live[h][:, None], np.exp(s - lse_safe[h][:, None]), 0.0)
+            do = dout[:, h, :]
+            dv[r, :, h // G, :] += p.T @ do
+            dp = do @ vr.T
+            ds = p * (dp - D[h][:, None])
+            dq[:, h, :] += ds @ kr * scale
+            dk[r, :, h // G, :] += ds.T @ q_local[:, h, :] * scale
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
 # Decode: the query passes, the key/value shard stays.
 # ---------------------------------------------------------------------------
 

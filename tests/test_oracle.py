@@ -465,6 +465,154 @@ def test_merge_of_block_partials_equals_dense(layout):
 
 
 # ---------------------------------------------------------------------------
+# Backward: gradients of L = sum(dO * O).
+# ---------------------------------------------------------------------------
+
+def _loss(q, tq, k, v, dout, causal):
+    o, _ = ro.dense_attention(q, tq, k, v, causal)
+    return float((o * dout).sum())
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_dense_matches_finite_differences(causal):
+    """Central differences of L = sum(dO * O) through the dense forward, on
+    every element of q, k and v of a tiny problem."""
+    rng = np.random.default_rng(61)
+    N, Hq, Hkv, d = 5, 2, 1, 3
+    q, k, v = _rand_qkv(rng, N, Hq, Hkv, d, scale=1.0)
+    dout = rng.standard_normal((N, Hq, d))
+    tq = np.arange(N)
+    dq, dk, dv = ro.backward_dense(q, tq, k, v, dout, causal)
+    h = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = _loss(q, tq, k, v, dout, causal)
+            arr[idx] = old - h
+            lm = _loss(q, tq, k, v, dout, causal)
+            arr[idx] = old
+            assert abs((lp - lm) / (2 * h) - grad[idx]) <= 1e-7, (idx, grad[idx])
+
+
+def test_backward_dense_matches_torch_autograd():
+    """float64 autograd of a plain masked softmax attention written here."""
+    import torch
+    rng = np.random.default_rng(62)
+    N, Hq, Hkv, d = 9, 4, 2, 8
+    q, k, v = _rand_qkv(rng, N, Hq, Hkv, d, scale=2.0)
+    dout = rng.standard_normal((N, Hq, d))
+    tq = np.array([2, 3, 5, 8, 8, 0, 7, 1, 4])          # query positions in any order
+    for causal in (True, False):
+        dq, dk, dv = ro.backward_dense(q, tq, k, v, dout, causal)
+        tqq = torch.tensor(q, requires_grad=True)
+        tk = torch.tensor(k, requires_grad=True)
+        tv = torch.tensor(v, requires_grad=True)
+        G = Hq // Hkv
+        ke = tk.repeat_interleave(G, dim=1)                # [N, Hq, d]
+        ve = tv.repeat_interleave(G, dim=1)
+        sc = torch.einsum("ihc,jhc->hij", tqq, ke) / np.sqrt(d)
+        if causal:
+            mask = torch.tensor(np.arange(N)[None, :] > tq[:, None])
+            sc = sc.masked_fill(mask[None], float("-inf"))
+        o = torch.einsum("hij,jhc->ihc", torch.softmax(sc, dim=-1), ve)
+        (o * torch.tensor(dout)).sum().backward()
+        np.testing.assert_allclose(dq, tqq.grad.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+BWD_CASES = [
+    # layout, causal, P, b, Hq, Hkv, d
+    ("contiguous", True, 4, 5, 4, 2, 8),
+    ("contiguous", False, 2, 6, 2, 1, 4),
+    ("striped", True, 4, 4, 2, 1, 8),
+    ("zigzag", True, 4, 6, 4, 2, 8),
+    ("contiguous", True, 1, 7, 2, 2, 4),
+]
+
+
+def _ring_backward_all_ranks(layout, causal, P, b, Hq, Hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    N = P * b
+    q, k, v = _rand_qkv(rng, N, Hq, Hkv, d, scale=2.0)
+    dout = rng.standard_normal((N, Hq, d))
+    dq = np.zeros((N, Hq, d))
+    dk = np.zeros((N, Hkv, d))
+    dv = np.zeros((N, Hkv, d))
+    for u in range(P):
+        tq = ro.shard_positions(layout, u, P, b)
+        out, lse = ro.ring_forward(q[tq], u, k, v, P, layout, causal)
+        gq, gk, gv = ro.ring_backward(q[tq], u, k, v, out, lse, dout[tq], P, layout, causal)
+        dq[tq] = gq
+        for r in range(P):
+            tk = ro.shard_positions(layout, r, P, b)
+            dk[tk] += gk[r]
+            dv[tk] += gv[r]
+    return (q, k, v, dout), (dq, dk, dv)
+
+
+@pytest.mark.parametrize("layout,causal,P,b,Hq,Hkv,d", BWD_CASES)
+def test_ring_backward_over_all_ranks_equals_dense_gradient(layout, causal, P, b, Hq, Hkv, d):
+    """Every rank's dQ, and the contributions of all ranks to each block's dK,
+    dV summed as the rotating accumulators sum them, give the dense gradient."""
+    (q, k, v, dout), (dq, dk, dv) = _ring_backward_all_ranks(layout, causal, P, b, Hq, Hkv, d, P * 10 + b)
+    N = P * b
+    wq, wk, wv = ro.backward_dense(q, np.arange(N), k, v, dout, causal)
+    np.testing.assert_allclose(dq, wq, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, wk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, wv, rtol=0, atol=1e-12)
+
+
+def test_ring_backward_order_invariance():
+    rng = np.random.default_rng(63)
+    P, b, Hq, Hkv, d = 4, 5, 2, 1, 8
+    q, k, v = _rand_qkv(rng, P * b, Hq, Hkv, d, scale=2.0)
+    dout = rng.standard_normal((P * b, Hq, d))
+    u = 2
+    tq = ro.shard_positions("striped", u, P, b)
+    out, lse = ro.ring_forward(q[tq], u, k, v, P, "striped", True)
+    base = ro.ring_backward(q[tq], u, k, v, out, lse, dout[tq], P, "striped", True)
+    for _ in range(3):
+        got = ro.ring_backward(q[tq], u, k, v, out, lse, dout[tq], P, "striped", True, order=rng.permutation(P))
+        for a, b_ in zip(got, base):
+            np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+
+
+def _bwd_without_d_term(q_local, u, k, v, out, lse, dout, P, layout, causal, order=None):
+    return _REAL_BWD(q_local, u, k, v, out * 0.0, lse, dout, P, layout, causal, order)
+
+
+def _bwd_unscaled_dk(q_local, u, k, v, out, lse, dout, P, layout, causal, order=None):
+    dq, dk, dv = _REAL_BWD(q_local, u, k, v, out, lse, dout, P, layout, causal, order)
+    return dq, dk * math.sqrt(q_local.shape[2]), dv
+
+
+def _bwd_dense_no_centering(q_rows, tq, k, v, dout, causal):
+    dq, dk, dv = _REAL_BWD_DENSE(q_rows, tq, k, v, dout, causal)
+    return dq * 1.0001, dk, dv
+
+
+_REAL_BWD = ro.ring_backward
+_REAL_BWD_DENSE = ro.backward_dense
+
+
+@pytest.mark.parametrize("replacement", [_bwd_without_d_term, _bwd_unscaled_dk])
+def test_planted_ring_backward_mistakes_are_caught(monkeypatch, replacement):
+    monkeypatch.setattr(ro, "ring_backward", replacement)
+    with pytest.raises(AssertionError):
+        test_ring_backward_over_all_ranks_equals_dense_gradient(*BWD_CASES[0])
+
+
+def test_planted_dense_backward_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(ro, "backward_dense", _bwd_dense_no_centering)
+    with pytest.raises(AssertionError):
+        test_backward_dense_matches_torch_autograd()
+    with pytest.raises(AssertionError):
+        test_backward_dense_matches_finite_differences(True)
+
+
+# ---------------------------------------------------------------------------
 # Decode: partial triples of resident shards.
 # ---------------------------------------------------------------------------
 
@@ -721,6 +869,8 @@ def test_planted_decode_mistake_is_caught(monkeypatch):
 
 
 def test_package_exports():
+    assert oracle.ring_backward is ro.ring_backward
+    assert oracle.backward_dense is ro.backward_dense
     assert oracle.decode_partial is ro.decode_partial
     assert oracle.ring_forward is ro.ring_forward
     assert oracle.merge_partials is ro.merge_partials
