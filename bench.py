@@ -15,11 +15,13 @@ kernel inside the timed region.  ``cpu_baseline`` times the fp64 oracle on the
 host cores on a bounded sample of query rows of the same workload.
 ``merge_kernel`` and ``decode_kernel`` report the two HBM-bound kernels (the
 triple merge; the pass-Q decode partial of one resident shard) as achieved GB/s
-against 8 TB/s.
+against 8 TB/s; ``backward`` reports the backward ring of a workload's rank as
+useful TFLOP/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--cpu-seconds S] [--no-cpu-baseline] [--no-merge]
                        [--no-decode] [--decode-workload NAME] [--decode-only]
+                       [--no-backward] [--backward-workload NAME] [--backward-only]
 """
 
 from __future__ import annotations
@@ -255,6 +257,60 @@ def measure_decode(name: str = "decode-31k-gqa64", reps: int = 20) -> dict:
             "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "calls": t["decode_calls"]}
 
 
+def backward_useful_flops(pairs: int, d: int, heads: int) -> float:
+    """The backward of attention with recomputed scores: S = Q K^T again, then
+    dV = P^T dO, dP = dO V^T, dQ = dS K, dK = dS^T Q: five contractions of
+    2*d FLOPs per allowed pair and head, 10*d (2.5x the forward's)."""
+    return 10.0 * d * pairs * heads
+
+
+def measure_backward(name: str = "32k-contiguous-causal", reps: int = 3) -> dict:
+    """Time ringattn_backward for the workload's rank (inputs: the GPU
+    forward's O and LSE, a seeded upstream gradient) and report useful
+    TFLOP/s per call and per step-kernel time against the bf16 peak."""
+    import torch
+
+    import ring_attention_block_step_amd as ra
+    import workloads as wl
+
+    w = wl.WORKLOADS[name]
+    rank = w.ranks[-1]
+    k_glob, v_glob = wl.global_kv(w)
+    idx = ra.shard_index(w.N, w.P, w.layout, rank)
+    q = wl.query_rows(w, idx.numpy()).cuda()
+    do = wl.token_rows(w.seed, "do", idx.numpy(), w.Hq, w.d, "normal", 1.0, w.torch_dtype).cuda()
+    kp = ra.pack_shards(k_glob, w.P, w.layout).cuda()
+    vp = ra.pack_shards(v_glob, w.P, w.layout).cuda()
+    del k_glob, v_glob
+    out, lse = ra.forward(q, kp, vp, P=w.P, rank=rank, causal=w.causal, layout=w.layout)
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(kp.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(kp.shape, dtype=torch.float32, device="cuda")
+    ra.backward(q, kp, vp, out, lse, do, P=w.P, rank=rank, causal=w.causal, layout=w.layout, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ra.timing_collect_backward()
+    ra.timing_enable(True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        ra.backward(q, kp, vp, out, lse, do, P=w.P, rank=rank, causal=w.causal, layout=w.layout, dq=dq, dk=dk,
+                    dv=dv)
+    t1.record()
+    torch.cuda.synchronize()
+    ra.timing_enable(False)
+    t = ra.timing_collect_backward()
+    ms = t0.elapsed_time(t1) / reps
+    flops = backward_useful_flops(useful_pairs(w.layout, rank, w.P, w.b, w.causal), w.d, w.Hq)
+    kern_ms = t["step_ms"] / reps
+    return {"workload": name, "rank": rank, "useful_flops": flops, "ms_per_call": ms,
+            "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "kernels": "bwd_dkdv_kernel<128>+bwd_dq_kernel<128>", "kernel_ms_per_call": kern_ms,
+            "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "frac": flops / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "visits_per_call": t["step_launches"] / reps,
+            "note": "useful = 5 contractions per allowed pair; the kernels run 7 (the dQ kernel recomputes S, dP)"}
+
+
 def copy_calibration(nbytes: int, reps: int = 3) -> None:
     """A plain device copy of known size (torch's copy kernel), for scaling the
     FETCH_SIZE / WRITE_SIZE counters of other kernels."""
@@ -286,6 +342,11 @@ def main(argv=None) -> int:
                     help="decode workload of the decode-kernel measurement")
     ap.add_argument("--decode-only", action="store_true",
                     help="only run the decode-kernel measurement and print its JSON object")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--backward-workload", default="32k-contiguous-causal",
+                    help="workload of the backward measurement")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only run the backward measurement and print its JSON object")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -307,6 +368,9 @@ def main(argv=None) -> int:
         return 3
     if args.decode_only:
         print(json.dumps(measure_decode(args.decode_workload)), flush=True)
+        return 0
+    if args.backward_only:
+        print(json.dumps(measure_backward(args.backward_workload, reps=max(1, args.steps))), flush=True)
         return 0
     if args.copy_bytes:
         copy_calibration(args.copy_bytes)
@@ -374,6 +438,7 @@ def main(argv=None) -> int:
 
     merge = None if args.no_merge else measure_merge()
     decode = None if args.no_decode else measure_decode(args.decode_workload)
+    backward = None if args.no_backward else measure_backward(args.backward_workload)
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
@@ -401,6 +466,7 @@ def main(argv=None) -> int:
         "parity_sample": parity,
         "merge_kernel": merge,
         "decode_kernel": decode,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -87,6 +87,40 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
                          int causal, int layout, void* stream);
 
 /*
+ * ringattn_backward -- rank `rank`'s share of the backward ring (the
+ * transformer-math page (aicassindra.com), "The backward pass costs a second
+ * ring"): the P key/value blocks visit again in the forward's ring order; for
+ * each visit the scores are rebuilt from the saved LSE rather than stored,
+ *   P = exp(S - LSE),  D = rowsum(dO * O),  dS = P * (dP - D),  dP = dO V^T,
+ * dQ of the rank's rows collects dS K / sqrt(d_h) over all visits, and the
+ * visiting block's gradient accumulators collect this rank's contribution
+ * dK_r += dS^T Q / sqrt(d_h), dV_r += P^T dO, as they would while rotating
+ * with the block.  Gradients are of L = sum(dO * O) for the O of
+ * ringattn_forward with the same shapes, mask and layout.
+ *
+ *  q, out, dout [b, Hq, d_h]     bf16: the rank's query rows, the forward's O
+ *                                and the upstream gradient (read only)
+ *  lse          [Hq, b]          fp32, the forward's LSE (natural log)
+ *  k, v         [P, b, Hkv, d_h] bf16, every shard as for ringattn_forward
+ *  dq           [b, Hq, d_h]     fp32, dL/dQ of the rank's rows (written)
+ *  dk, dv       [P, b, Hkv, d_h] fp32, ADDED TO: this rank's contribution to
+ *                                every shard's dL/dK and dL/dV (blocks the
+ *                                rank never sees get nothing).  Zero them
+ *                                before the first rank; after all P ranks
+ *                                they hold the full gradients.
+ *  N, P, rank, Hq, Hkv, d_h, causal, layout as for ringattn_forward.
+ *  Every pointer is required and 16-byte aligned.
+ *
+ * The library allocates its workspace (the query rows' packed tiles and two
+ * packed key/value slots) stream-ordered on `stream`; the slot of visit s+1 is
+ * packed on the library's second stream while visit s computes.
+ */
+int ringattn_backward(const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                      int64_t N, int P, int rank, int Hq, int Hkv, int d_h,
+                      int causal, int layout, void* stream);
+
+/*
  * ringattn_merge -- combine `nparts` partial (m, z, y) triples of the same
  * rows with one rescale-and-add (the transformer-math page, "The ring is a
  * prefill algorithm": each shard returns a partial (m, l, o) and one small
@@ -154,6 +188,10 @@ const char* ringattn_last_error(void);
 int ringattn_timing_enable(int enable);
 int ringattn_timing_collect(double* step_ms, int64_t* step_launches,
                             double* merge_ms, int64_t* merge_launches);
+
+/* Same for the step kernels of ringattn_backward (the dK/dV and dQ kernels of
+ * each visit together): summed duration (ms) and number of visits. */
+int ringattn_timing_collect_backward(double* step_ms, int64_t* step_launches);
 
 /* Same for ringattn_decode_partial calls: summed duration (ms) of the decode
  * kernels of each call (chunk and combine kernels together) and the number of

@@ -8,7 +8,8 @@ fallback, and using any entry point without the built library raises.
 
 Names follow the C ABI: ``forward`` (``ringattn_forward`` for bf16,
 ``ringattn_forward_f32`` for fp32), ``merge`` (``ringattn_merge``),
-``decode_partial`` (``ringattn_decode_partial``).
+``decode_partial`` (``ringattn_decode_partial``), ``backward``
+(``ringattn_backward``).
 """
 
 from __future__ import annotations
@@ -18,17 +19,18 @@ import os
 
 import torch
 
-__all__ = ["forward", "merge", "decode_partial", "shard_index", "pack_shards", "lib", "RingAttnError",
-           "timing_enable", "timing_collect", "timing_collect_decode", "set_serial_hops", "version", "SYMBOLS",
+__all__ = ["forward", "backward", "merge", "decode_partial", "shard_index", "pack_shards", "lib", "RingAttnError",
+           "timing_enable", "timing_collect", "timing_collect_decode", "timing_collect_backward", "set_serial_hops", "version", "SYMBOLS",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
 LAYOUTS = {"contiguous": 0, "striped": 1, "zigzag": 2}
 
 # Every symbol include/ringattn.h declares.
-SYMBOLS = ("ringattn_forward", "ringattn_forward_f32", "ringattn_merge", "ringattn_decode_partial",
-           "ringattn_status_string", "ringattn_last_error", "ringattn_timing_enable", "ringattn_timing_collect",
-           "ringattn_timing_collect_decode", "ringattn_set_serial_hops", "ringattn_version")
+SYMBOLS = ("ringattn_forward", "ringattn_forward_f32", "ringattn_backward", "ringattn_merge",
+           "ringattn_decode_partial", "ringattn_status_string", "ringattn_last_error", "ringattn_timing_enable",
+           "ringattn_timing_collect", "ringattn_timing_collect_backward", "ringattn_timing_collect_decode",
+           "ringattn_set_serial_hops", "ringattn_version")
 
 _lib = None
 
@@ -55,6 +57,11 @@ def lib() -> ctypes.CDLL:
     L.ringattn_forward_f32.restype = i32
     L.ringattn_merge.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, i32, f32p, vp]
     L.ringattn_merge.restype = i32
+    L.ringattn_backward.argtypes = [vp, vp, vp, vp, f32p, vp, f32p, f32p, f32p, i64, i32, i32, i32, i32, i32, i32,
+                                    i32, vp]
+    L.ringattn_backward.restype = i32
+    L.ringattn_timing_collect_backward.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.ringattn_timing_collect_backward.restype = i32
     L.ringattn_decode_partial.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp]
     L.ringattn_decode_partial.restype = i32
     L.ringattn_status_string.argtypes = [i32]
@@ -173,6 +180,46 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, rank: 
     return out, lse
 
 
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, *, P: int, rank: int, causal: bool, layout: str = "contiguous",
+             dk: torch.Tensor | None = None, dv: torch.Tensor | None = None, dq: torch.Tensor | None = None):
+    """Rank ``rank``'s share of the backward ring.
+
+    q, out, dout: [b, Hq, d] bf16; lse: [Hq, b] fp32 (the forward's); k, v:
+    [P, b, Hkv, d] bf16.  Returns (dq [b, Hq, d], dk, dv [P, b, Hkv, d]), all
+    fp32.  dk and dv are ADDED TO when given (zeros are made otherwise), so
+    passing the same tensors for every rank accumulates the full gradients.
+    Asynchronous on the current stream of q's device.
+    """
+    L = lib()
+    ts = (q, k, v, out, dout)
+    _need(all(t.is_cuda and t.device == q.device for t in ts + (lse,)), "all tensors must be on q's device")
+    _need(all(t.dtype == torch.bfloat16 for t in ts), "q, k, v, out, dout must be bfloat16")
+    _need(lse.dtype == torch.float32, "lse must be float32")
+    _need(all(t.is_contiguous() for t in ts + (lse,)), "tensors must be contiguous")
+    _need(q.dim() == 3 and k.dim() == 4 and v.shape == k.shape and out.shape == q.shape and dout.shape == q.shape,
+          "q, out, dout [b, Hq, d]; k, v [P, b, Hkv, d]")
+    b, Hq, d = q.shape
+    _need(k.shape[0] == P and k.shape[1] == b and k.shape[3] == d, "k, v must be [P, b, Hkv, d] matching q")
+    _need(tuple(lse.shape) == (Hq, b), "lse must be [Hq, b]")
+    _need(layout in LAYOUTS, f"layout must be one of {sorted(LAYOUTS)}")
+    if dq is None:
+        dq = torch.empty((b, Hq, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    _need(dq.shape == q.shape and dq.dtype == torch.float32 and dq.is_contiguous(), "dq must be float32 [b, Hq, d]")
+    for t, name in ((dk, "dk"), (dv, "dv")):
+        _need(t.shape == k.shape and t.dtype == torch.float32 and t.is_contiguous() and t.device == q.device,
+              f"{name} must be float32 [P, b, Hkv, d] on q's device")
+    with torch.cuda.device(q.device):
+        _check(L.ringattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), P * b, P, rank, Hq, k.shape[2], d, int(bool(causal)), LAYOUTS[layout],
+                                   _stream(q.device)))
+    return dq, dk, dv
+
+
 def merge(m: torch.Tensor, z: torch.Tensor, y: torch.Tensor, *, out_dtype=torch.bfloat16,
           out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True):
     """Combine partial triples: m, z [n, Hq, rows], y [n, rows, Hq, d], fp32.
@@ -247,6 +294,13 @@ def timing_collect() -> dict:
     sn, mn = ctypes.c_int64(), ctypes.c_int64()
     _check(lib().ringattn_timing_collect(ctypes.byref(sm), ctypes.byref(sn), ctypes.byref(mm), ctypes.byref(mn)))
     return {"step_ms": sm.value, "step_launches": sn.value, "merge_ms": mm.value, "merge_launches": mn.value}
+
+
+def timing_collect_backward() -> dict:
+    """Summed backward step-kernel durations (ms) and visit count since the last collect."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib().ringattn_timing_collect_backward(ctypes.byref(ms), ctypes.byref(n)))
+    return {"step_ms": ms.value, "step_launches": n.value}
 
 
 def timing_collect_decode() -> dict:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libringattn.so")
-SOURCES = ["driver.hip", "pack.hip", "step_bf16.hip", "step_f32.hip", "merge.hip", "decode.hip"]
+SOURCES = ["driver.hip", "pack.hip", "step_bf16.hip", "step_f32.hip", "merge.hip", "decode.hip", "backward.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code.  Private

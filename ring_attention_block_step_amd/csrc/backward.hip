@@ -1,0 +1,523 @@
+// Backward ring on bf16 inputs: rank u's share of the gradient of
+// L = sum(dO * O) ("The backward pass costs a second ring", the
+// transformer-math page (aicassindra.com)): the key/value blocks visit again,
+// the [b, b] scores of each visit are rebuilt from the saved LSE instead of
+// being stored, dQ_u stays on the device, and each visiting block's dK, dV
+// receive the device's contribution as it passes.  Per visit r:
+//   P = exp(S - LSE),  D = rowsum(dO * O),  dV_r += P^T dO,  dP = dO V_r^T,
+//   dS = P * (dP - D),  dQ += dS K_r / sqrt(d),  dK_r += dS^T Q / sqrt(d).
+// No running maximum is needed: LSE is the exact normaliser, so every
+// probability is at most 1.
+//
+// Kernels (v_mfma_f32_32x32x16_bf16, fp32 accumulation, P and dS rounded to
+// bf16 only as MFMA operands):
+//   bwd_prep_kernel   once per call: D and LSE (log2 units) per query row,
+//                     and the query items' tiles (32 rows of one head):
+//                     Q and dO row-major (MFMA A operand of S and dP) and
+//                     Q^T, dO^T transposed with the in-group query order of
+//                     the score accumulator (A operand of dK^T and dV^T);
+//   bwd_dkdv_kernel   per visit: a wave owns 32 keys of the block (K and V
+//                     fragments in registers) and runs over every query item
+//                     that sees them: S = Q K^T, dP = dO V^T, then
+//                     dV^T += dO^T P and dK^T += Q^T dS; at the end it adds
+//                     into the caller's dK_r, dV_r;
+//   bwd_dq_kernel     per visit: a wave owns one query item (Q and dO
+//                     fragments in registers) and runs over the block's key
+//                     tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T,
+//                     with K, V and K^T tiles staged in LDS.
+#include "internal.h"
+
+namespace ringattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_t;
+typedef const bf16x8 __attribute__((address_space(3)))* lds_frag_ptr;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Storage position kappa (0..15) inside a group of 16 holds element
+// perm(kappa): the order in which a 32x32 accumulator hands its rows to a
+// lane (registers 8g .. 8g+7 of lane l cover rows 16g + perm(8*(l/32) + e)).
+__host__ __device__ inline int perm16(int kappa) { return (kappa & 3) | ((kappa & 4) << 1) | ((kappa & 8) >> 1); }
+
+// Query item block (32 rows of one query head), copied to LDS verbatim:
+//   [Q  row-major 32 x D][dO row-major][Q^T D x 32][dO^T D x 32][stats 1 KB]
+// row-major: 16-byte chunk c (d = 8c .. 8c+7) of row j at c*512 + j*16;
+// transposed: row d, chunk c (queries 8c .. 8c+7 in storage order, query
+// 16*(c/2) + perm16(8*(c%2) + e) at element e) at c*D*16 + d*16;
+// stats: lse2[32] (LSE * log2 e; +inf for a row that saw no key), then D[32].
+template <int D>
+struct Item {
+  static constexpr int TILE = 32 * D * 2;
+  static constexpr int QK = 0, DOK = TILE, QV = 2 * TILE, DOV = 3 * TILE, STATS = 4 * TILE;
+  static constexpr int BYTES = 4 * TILE + 1024;
+  static constexpr int CHUNKS = BYTES / 1024;
+};
+__host__ __device__ inline int rowtile_off(int row, int chunk) { return chunk * 512 + row * 16; }
+template <int D>
+__host__ __device__ inline int coltile_off(int drow, int chunk) { return chunk * (D * 16) + drow * 16; }
+
+// Key tile block of the dQ kernel's slot (64 keys of one key/value head):
+//   [K row-major (key_tile_off)][V row-major (key_tile_off)][K^T (val_tile_off)]
+template <int D>
+struct KBlock {
+  static constexpr int TILE = kKeyTile * D * 2;
+  static constexpr int K = 0, V = TILE, KT = 2 * TILE;
+  static constexpr int BYTES = 3 * TILE;
+  static constexpr int CHUNKS = BYTES / 1024;
+};
+
+__device__ __forceinline__ void wait_all_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// Whether key j of the visiting block may be seen by local query row i (see
+// BlockMask); rows and keys at or beyond b never are.
+__device__ __forceinline__ bool allowed(const BwdArgs& a, int i, int j) {
+  return i < a.b && j < a.kend && i >= a.qbeg && (a.shift < 0 || j <= i - a.shift);
+}
+
+// ---------------------------------------------------------------------------
+// Preparation: stats and query item tiles.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int CPR = D / 8;
+  constexpr int VS = D + 8;               // LDS pitch (elements) of the staging rows
+  __shared__ uint16_t sq[32 * VS], sd[32 * VS];
+  const int pb = blockIdx.x, hq = blockIdx.y;
+  const int q0 = pb * 32;
+  unsigned char* blk = reinterpret_cast<unsigned char*>(a.items) + ((size_t)hq * a.npb + pb) * Item<D>::BYTES;
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
+  const uint16_t* dout = reinterpret_cast<const uint16_t*>(a.dout);
+
+  for (int c = threadIdx.x; c < 32 * CPR; c += 256) {
+    const int row = c / CPR, cc = c % CPR;
+    const int i = q0 + row;
+    uint4 qv = make_uint4(0, 0, 0, 0), dv = make_uint4(0, 0, 0, 0);
+    if (i < a.b) {
+      const size_t src = ((size_t)i * a.Hq + hq) * D + cc * 8;
+      qv = *reinterpret_cast<const uint4*>(q + src);
+      dv = *reinterpret_cast<const uint4*>(dout + src);
+    }
+    *reinterpret_cast<uint4*>(blk + Item<D>::QK + rowtile_off(row, cc)) = qv;
+    *reinterpret_cast<uint4*>(blk + Item<D>::DOK + rowtile_off(row, cc)) = dv;
+    *reinterpret_cast<uint2*>(sq + row * VS + cc * 8) = make_uint2(qv.x, qv.y);
+    *reinterpret_cast<uint2*>(sq + row * VS + cc * 8 + 4) = make_uint2(qv.z, qv.w);
+    *reinterpret_cast<uint2*>(sd + row * VS + cc * 8) = make_uint2(dv.x, dv.y);
+    *reinterpret_cast<uint2*>(sd + row * VS + cc * 8 + 4) = make_uint2(dv.z, dv.w);
+  }
+  // Stats: D = rowsum(dO * O) in fp32 from the bf16 values, LSE in log2 units.
+  if (threadIdx.x < 32) {
+    const int row = threadIdx.x, i = q0 + row;
+    float dsum = 0.f, l2 = INFINITY;
+    if (i < a.b) {
+      const uint16_t* o = reinterpret_cast<const uint16_t*>(a.out) + ((size_t)i * a.Hq + hq) * D;
+      const uint16_t* g = dout + ((size_t)i * a.Hq + hq) * D;
+      for (int c = 0; c < D; ++c)
+        dsum = fmaf(__uint_as_float((uint32_t)o[c] << 16), __uint_as_float((uint32_t)g[c] << 16), dsum);
+      const float lse = a.lse[(size_t)hq * a.b + i];
+      l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+    }
+    float* st = reinterpret_cast<float*>(blk + Item<D>::STATS);
+    st[row] = l2;
+    st[32 + row] = dsum;
+  }
+  __syncthreads();
+  // Transposed tiles: row d, chunk c holds queries in storage order.
+  for (int c = threadIdx.x; c < D * 4; c += 256) {
+    const int d = c / 4, ch = c % 4;
+    uint32_t wq[4], wd[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      uint32_t pq[2], pd[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int kappa = 8 * (ch % 2) + e + x;
+        const int row = 16 * (ch / 2) + perm16(kappa);
+        pq[x] = sq[row * VS + d];
+        pd[x] = sd[row * VS + d];
+      }
+      wq[e / 2] = pq[0] | (pq[1] << 16);
+      wd[e / 2] = pd[0] | (pd[1] << 16);
+    }
+    *reinterpret_cast<uint4*>(blk + Item<D>::QV + coltile_off<D>(d, ch)) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+    *reinterpret_cast<uint4*>(blk + Item<D>::DOV + coltile_off<D>(d, ch)) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  }
+}
+
+// Slot of the dQ kernel: per key/value head, tiles of 64 keys holding K and V
+// row-major and K^T transposed (keys in storage order); rows b .. bpad-1 zero.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                       unsigned char* __restrict__ slot, int b, int bpad, int Hkv) {
+  constexpr int T = kKeyTile;
+  constexpr int CPR = D / 8;
+  constexpr int VS = D + 8;
+  __shared__ uint16_t ks[T * VS];
+  const int t = blockIdx.x, h = blockIdx.y;
+  const int ntiles = bpad / T;
+  unsigned char* blk = slot + ((size_t)h * ntiles + t) * KBlock<D>::BYTES;
+  for (int c = threadIdx.x; c < T * CPR; c += 256) {
+    const int row = c / CPR, cc = c % CPR;
+    const int j = t * T + row;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (j < b) {
+      const size_t src = ((size_t)j * Hkv + h) * D + cc * 8;
+      kv = *reinterpret_cast<const uint4*>(k + src);
+      vv = *reinterpret_cast<const uint4*>(v + src);
+    }
+    *reinterpret_cast<uint4*>(blk + KBlock<D>::K + key_tile_off(row, cc)) = kv;
+    *reinterpret_cast<uint4*>(blk + KBlock<D>::V + key_tile_off(row, cc)) = vv;
+    *reinterpret_cast<uint2*>(ks + row * VS + cc * 8) = make_uint2(kv.x, kv.y);
+    *reinterpret_cast<uint2*>(ks + row * VS + cc * 8 + 4) = make_uint2(kv.z, kv.w);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < T * CPR; c += 256) {
+    const int d = c / (T / 8);
+    const int k0 = (c % (T / 8)) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      uint32_t pair[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int kappa = k0 + e + x;
+        pair[x] = ks[((kappa & ~15) + perm16(kappa & 15)) * VS + d];
+      }
+      w[e / 2] = pair[0] | (pair[1] << 16);
+    }
+    *reinterpret_cast<uint4*>(blk + KBlock<D>::KT + val_tile_off<D>(d, k0 / 8)) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Direct global -> LDS copy of `chunks` 1 KB chunks, spread over `waves` waves.
+__device__ __forceinline__ void load_chunks(const unsigned char* g, lds_t* l, int chunks, int waves, int wave,
+                                            int lane) {
+  for (int c = wave; c < chunks; c += waves)
+    __builtin_amdgcn_global_load_lds(g + c * 1024 + lane * 16, l + c * 1024, 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const f32x2 pp = {s[base + e], s[base + e + 1]};
+    const bf16x2 pk = __builtin_convertvector(pp, bf16x2);
+    r[e] = pk[0];
+    r[e + 1] = pk[1];
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV of the visiting block.
+// ---------------------------------------------------------------------------
+
+constexpr int kDkvWaves = 4;   // 4 waves x 32 keys = 128 keys per workgroup
+
+template <int D>
+__global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  using IT = Item<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[2 * IT::BYTES];
+  lds_t* smem = (lds_t*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int kvh = blockIdx.y;
+  const int wk0 = blockIdx.x * (32 * kDkvWaves);
+  const int k0 = wk0 + wave * 32;
+  const int key = k0 + l32;
+
+  // Query rows that may see any key of the workgroup: from q_lo on.
+  if (wk0 >= a.kend) return;
+  int q_lo = a.qbeg;
+  if (a.shift >= 0) q_lo = max(q_lo, wk0 + a.shift);
+  const int pb_lo = q_lo / 32;
+  const int n_items = pb_lo < a.npb ? (a.npb - pb_lo) * a.G : 0;
+
+  // K and V fragments of the wave's 32 keys (B operand: key l32, d = 16ks + 8hi ..).
+  bf16x8 kf[KS], vf[KS];
+  {
+    const bool kin = key < a.b;
+    const size_t base = ((size_t)(kin ? key : 0) * a.Hkv + kvh) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 zk, zv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zk[e] = zv[e] = (__bf16)0.0f;
+      kf[ks] = kin ? *reinterpret_cast<const bf16x8*>(a.k + base + ks * 16 + hi * 8) : zk;
+      vf[ks] = kin ? *reinterpret_cast<const bf16x8*>(a.v + base + ks * 16 + hi * 8) : zv;
+    }
+  }
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.f;
+
+  auto item_src = [&](int it) {
+    const int pb = pb_lo + it / a.G;
+    const int hq = kvh * a.G + it % a.G;
+    return reinterpret_cast<const unsigned char*>(a.items) + ((size_t)hq * a.npb + pb) * IT::BYTES;
+  };
+  if (n_items > 0) load_chunks(item_src(0), smem, IT::CHUNKS, kDkvWaves, wave, lane);
+  wait_all_and_sync();
+
+  for (int it = 0; it < n_items; ++it) {
+    lds_t* cur = smem + (it & 1) * IT::BYTES;
+    if (it + 1 < n_items) load_chunks(item_src(it + 1), smem + ((it + 1) & 1) * IT::BYTES, IT::CHUNKS, kDkvWaves, wave, lane);
+    const int q0 = (pb_lo + it / a.G) * 32;
+
+    // S = Q K^T and dP = dO V^T: lane holds key l32, register r query
+    // 8(r/4) + 4hi + r%4.
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 qa = *reinterpret_cast<lds_frag_ptr>(cur + IT::QK + rowtile_off(l32, ks * 2 + hi));
+      const bf16x8 da = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOK + rowtile_off(l32, ks * 2 + hi));
+      s = mfma(qa, kf[ks], s);
+      dp = mfma(da, vf[ks], dp);
+    }
+    // P = exp2(S log2e/sqrt(d) - lse2), dS = P (dP - D); masked entries 0.
+    typedef const __attribute__((address_space(3))) float lds_f32;
+    typedef const f32x4 __attribute__((address_space(3)))* lds_f4_ptr;
+    lds_f32* st = (lds_f32*)(cur + IT::STATS);
+    f32x16 p, ds;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4 l2 = *(lds_f4_ptr)(st + 8 * rg + 4 * hi);
+      const f32x4 dd = *(lds_f4_ptr)(st + 32 + 8 * rg + 4 * hi);
+      const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+      const float dvv[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = rg * 4 + x;
+        const int qi = q0 + 8 * rg + 4 * hi + x;
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -lv[x]));
+        pv = allowed(a, qi, key) ? pv : 0.f;
+        p[r] = pv;
+        ds[r] = pv * (dp[r] - dvv[x]);
+      }
+    }
+    const bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
+    const bf16x8 db0 = pack8(ds, 0), db1 = pack8(ds, 8);
+    // dV^T += dO^T P and dK^T += Q^T dS (A: transposed tiles, row d = 32dt + l32).
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int drow = dt * 32 + l32;
+      const bf16x8 o0 = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOV + coltile_off<D>(drow, 0 + hi));
+      const bf16x8 o1 = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOV + coltile_off<D>(drow, 2 + hi));
+      const bf16x8 q0f = *reinterpret_cast<lds_frag_ptr>(cur + IT::QV + coltile_off<D>(drow, 0 + hi));
+      const bf16x8 q1f = *reinterpret_cast<lds_frag_ptr>(cur + IT::QV + coltile_off<D>(drow, 2 + hi));
+      dv[dt] = mfma(o0, pb0, dv[dt]);
+      dv[dt] = mfma(o1, pb1, dv[dt]);
+      dk[dt] = mfma(q0f, db0, dk[dt]);
+      dk[dt] = mfma(q1f, db1, dk[dt]);
+    }
+    wait_all_and_sync();
+  }
+
+  // Add into the caller's dK_r, dV_r: lane holds key l32, register r
+  // d = 32dt + 8(r/4) + 4hi + r%4 (4 consecutive d per group).
+  if (key >= a.b) return;
+  const float sc = a.scale;
+  float* dkr = a.dk + ((size_t)key * a.Hkv + kvh) * D;
+  float* dvr = a.dv + ((size_t)key * a.Hkv + kvh) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = dt * 32 + rg * 8 + hi * 4;
+      float4 gk = *reinterpret_cast<float4*>(dkr + d0);
+      float4 gv = *reinterpret_cast<float4*>(dvr + d0);
+      gk.x = fmaf(dk[dt][rg * 4 + 0], sc, gk.x);
+      gk.y = fmaf(dk[dt][rg * 4 + 1], sc, gk.y);
+      gk.z = fmaf(dk[dt][rg * 4 + 2], sc, gk.z);
+      gk.w = fmaf(dk[dt][rg * 4 + 3], sc, gk.w);
+      gv.x += dv[dt][rg * 4 + 0];
+      gv.y += dv[dt][rg * 4 + 1];
+      gv.z += dv[dt][rg * 4 + 2];
+      gv.w += dv[dt][rg * 4 + 3];
+      *reinterpret_cast<float4*>(dkr + d0) = gk;
+      *reinterpret_cast<float4*>(dvr + d0) = gv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ of the rank's query rows.
+// ---------------------------------------------------------------------------
+
+constexpr int kDqWaves = 8;    // 8 query items (32 rows each) per workgroup, one key/value head
+
+template <int D>
+__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  using KB = KBlock<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[2 * KB::BYTES];
+  lds_t* smem = (lds_t*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int kvh = blockIdx.x % a.Hkv;
+  const int wgi = a.dq_wgs_per_head - 1 - (int)(blockIdx.x / a.Hkv);
+  const int item = wgi * kDqWaves + wave;
+  const int items = a.G * a.npb;
+  const bool active = item < items;
+  const int it = active ? item : items - 1;
+  const int pblk = it / a.G;
+  const int hq = kvh * a.G + it % a.G;
+  const int q0 = pblk * 32;
+  const int qi = q0 + l32;
+
+  // Keys of the block a row range sees (a prefix, nondecreasing in the row).
+  auto keys_of = [&](int i) {
+    return i < a.qbeg ? 0 : (a.shift < 0 ? a.kend : max(0, min(a.kend, i + 1 - a.shift)));
+  };
+  const int last_item = min(wgi * kDqWaves + kDqWaves - 1, items - 1);
+  const int T = (keys_of(min((last_item / a.G) * 32 + 32, a.b) - 1) + kKeyTile - 1) / kKeyTile;
+  const int my_tiles = active ? (keys_of(min(q0 + 32, a.b) - 1) + kKeyTile - 1) / kKeyTile : 0;
+
+  // Q and dO fragments (B operand: query l32, d = 16ks + 8hi ..), row stats.
+  bf16x8 qf[KS], df[KS];
+  {
+    const int qc = min(qi, a.b - 1);
+    const size_t base = ((size_t)qc * a.Hq + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + base + ks * 16 + hi * 8);
+      df[ks] = *reinterpret_cast<const bf16x8*>(a.dout + base + ks * 16 + hi * 8);
+    }
+  }
+  const float* st = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(a.items) +
+                                                   ((size_t)hq * a.npb + pblk) * Item<D>::BYTES + Item<D>::STATS);
+  const float l2 = st[l32];
+  const float drow = st[32 + l32];
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+
+  const size_t head_tiles = (size_t)(a.bpad / kKeyTile);
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.kslot) + (size_t)kvh * head_tiles * KB::BYTES;
+  if (T > 0) load_chunks(kg, smem, KB::CHUNKS, kDqWaves, wave, lane);
+  wait_all_and_sync();
+
+  for (int t = 0; t < T; ++t) {
+    lds_t* cur = smem + (t & 1) * KB::BYTES;
+    if (t + 1 < T) load_chunks(kg + (size_t)(t + 1) * KB::BYTES, smem + ((t + 1) & 1) * KB::BYTES, KB::CHUNKS, kDqWaves, wave, lane);
+    if (t < my_tiles) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int row = half * 32 + l32;
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<lds_frag_ptr>(cur + KB::K + key_tile_off(row, ks * 2 + hi));
+          const bf16x8 va = *reinterpret_cast<lds_frag_ptr>(cur + KB::V + key_tile_off(row, ks * 2 + hi));
+          s = mfma(ka, qf[ks], s);
+          dp = mfma(va, df[ks], dp);
+        }
+        // Lane holds query qi, register r key t*64 + 32 half + 8(r/4) + 4hi + r%4.
+        f32x16 ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = t * kKeyTile + half * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -l2));
+          pv = allowed(a, qi, key) ? pv : 0.f;
+          ds[r] = pv * (dp[r] - drow);
+        }
+        const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 8);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int dr = dt * 32 + l32;
+          const bf16x8 k0f = *reinterpret_cast<lds_frag_ptr>(cur + KB::KT + val_tile_off<D>(dr, (half * 2 + 0) * 2 + hi));
+          const bf16x8 k1f = *reinterpret_cast<lds_frag_ptr>(cur + KB::KT + val_tile_off<D>(dr, (half * 2 + 1) * 2 + hi));
+          o[dt] = mfma(k0f, d0, o[dt]);
+          o[dt] = mfma(k1f, d1, o[dt]);
+        }
+      }
+    }
+    wait_all_and_sync();
+  }
+
+  if (!active || qi >= a.b) return;
+  // dQ row qi: lane holds d = 32dt + 8(r/4) + 4hi + r%4.
+  float* dq = a.dq + ((size_t)qi * a.Hq + hq) * D;
+  const float sc = a.scale;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = dt * 32 + rg * 8 + hi * 4;
+      float4 g = a.dq_accumulate ? *reinterpret_cast<float4*>(dq + d0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      g.x = fmaf(o[dt][rg * 4 + 0], sc, g.x);
+      g.y = fmaf(o[dt][rg * 4 + 1], sc, g.y);
+      g.z = fmaf(o[dt][rg * 4 + 2], sc, g.z);
+      g.w = fmaf(o[dt][rg * 4 + 3], sc, g.w);
+      *reinterpret_cast<float4*>(dq + d0) = g;
+    }
+}
+
+}  // namespace
+
+size_t bwd_item_bytes(int D) { return D == 128 ? Item<128>::BYTES : Item<64>::BYTES; }
+size_t bwd_kblock_bytes(int D) { return D == 128 ? KBlock<128>::BYTES : KBlock<64>::BYTES; }
+int bwd_dq_waves() { return kDqWaves; }
+
+hipError_t launch_bwd_prep(const BwdArgs& a, int D, hipStream_t st) {
+  const dim3 grid((unsigned)a.npb, (unsigned)a.Hq);
+  if (D == 128)
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pack(const __bf16* k_shard, const __bf16* v_shard, void* slot, int b, int bpad, int Hkv, int D,
+                           hipStream_t st) {
+  const dim3 grid((unsigned)(bpad / kKeyTile), (unsigned)Hkv);
+  const uint16_t* k = reinterpret_cast<const uint16_t*>(k_shard);
+  const uint16_t* v = reinterpret_cast<const uint16_t*>(v_shard);
+  unsigned char* s = static_cast<unsigned char*>(slot);
+  if (D == 128)
+    hipLaunchKernelGGL(bwd_pack_kernel<128>, grid, dim3(256), 0, st, k, v, s, b, bpad, Hkv);
+  else
+    hipLaunchKernelGGL(bwd_pack_kernel<64>, grid, dim3(256), 0, st, k, v, s, b, bpad, Hkv);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_step(const BwdArgs& a, int D, hipStream_t st) {
+  const dim3 gkv((unsigned)((a.b + 32 * kDkvWaves - 1) / (32 * kDkvWaves)), (unsigned)a.Hkv);
+  const dim3 gq((unsigned)(a.dq_wgs_per_head * a.Hkv));
+  if (D == 128) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gkv, dim3(64 * kDkvWaves), 0, st, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, gq, dim3(64 * kDqWaves), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gkv, dim3(64 * kDkvWaves), 0, st, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, gq, dim3(64 * kDqWaves), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ringattn

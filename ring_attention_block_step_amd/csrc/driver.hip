@@ -65,7 +65,7 @@ DeviceCtx g_dev[kMaxDevices];
 
 struct TimedLaunch {
   hipEvent_t begin, end;
-  int kind;  // 0 step, 1 merge, 2 decode
+  int kind;  // 0 step, 1 merge, 2 decode, 3 backward step
 };
 std::mutex g_timing_mu;
 bool g_timing = false;
@@ -176,11 +176,11 @@ int check_forward_args(const void* q, const void* k, const void* v, const void* 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: two key/value slots, then `extra_bytes` for the step kernels'
-// state (init() prepares it once per call).  step(slot, extra, i, mask,
-// carry_in, last, stream) runs visit i.
+// state (init() prepares it once per call).  step(slot, extra, i, r, mask,
+// carry_in, last, stream) runs visit i, of block r.
 template <typename StepFn, typename HopFn, typename InitFn>
 int run_ring(int P, int rank, int b, int causal, int layout, size_t slot_bytes, size_t extra_bytes, hipStream_t st,
-             HopFn hop_into, StepFn step, InitFn init) {
+             HopFn hop_into, StepFn step, InitFn init, int timing_kind = 0) {
   DeviceCtx* ctx = nullptr;
   int rc = device_ctx(&ctx);
   if (rc != RINGATTN_OK) return rc;
@@ -217,8 +217,8 @@ int run_ring(int P, int rank, int b, int causal, int layout, size_t slot_bytes, 
     }
     for (int i = 0; i < n; ++i) {
       if (i > 0 && !serial) HIP_TRY(hipStreamWaitEvent(st, ctx->ev_ready[i & 1], 0));
-      const int tix = timing_begin(st, 0);
-      HIP_TRY(step(slot[i & 1], extra, i, visits[i].mask, i > 0, i == n - 1, st));
+      const int tix = timing_begin(st, timing_kind);
+      HIP_TRY(step(slot[i & 1], extra, i, visits[i].r, visits[i].mask, i > 0, i == n - 1, st));
       timing_end(tix, st);
       if (i + 2 < n) {
         if (!serial) {
@@ -315,7 +315,7 @@ int ringattn_forward(const void* q, const void* k, const void* v, void* out, flo
   auto init = [&](char* extra, hipStream_t s) -> hipError_t {
     return launch_zero_flags(reinterpret_cast<int*>(extra + 2 * carry_bytes), grid, s);
   };
-  auto step = [&](char* slot, char* extra, int i, const BlockMask& mk, bool carry_in, bool last,
+  auto step = [&](char* slot, char* extra, int i, int, const BlockMask& mk, bool carry_in, bool last,
                   hipStream_t s) -> hipError_t {
     StepBf16Args x = a;
     char* cin = extra + (size_t)((i + 1) & 1) * carry_bytes;   // written by step i-1
@@ -360,7 +360,7 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
                           hipMemcpyDeviceToDevice, s);
   };
   auto init = [](char*, hipStream_t) -> hipError_t { return hipSuccess; };
-  auto step = [&](char* slot, char* carry, int, const BlockMask& mk, bool carry_in, bool last,
+  auto step = [&](char* slot, char* carry, int, int, const BlockMask& mk, bool carry_in, bool last,
                   hipStream_t s) -> hipError_t {
     StepF32Args a;
     a.q = q;
@@ -384,6 +384,68 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
     return launch_step_f32(a, D, s);
   };
   return run_ring(P, rank, b, causal, layout, slot_bytes, carry_bytes, st, hop, step, init);
+}
+
+int ringattn_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                      const void* dout, float* dq, float* dk, float* dv, int64_t N, int P, int rank, int Hq, int Hkv,
+                      int d_h, int causal, int layout, void* stream) {
+  int rc = check_forward_args(q, k, v, out, lse, N, P, rank, Hq, Hkv, d_h, causal, layout);
+  if (rc != RINGATTN_OK) return rc;
+  if (!lse || !dout || !dq || !dk || !dv) return fail(RINGATTN_EINVAL, "lse, dout, dq, dk and dv must be non-null");
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(RINGATTN_EINVAL, "dout, dq, dk and dv must be 16-byte aligned");
+  const int b = (int)(N / P);
+  const int D = d_h;
+  const int G = Hq / Hkv;
+  const int bpad = (int)padded_rows(b);
+  const int npb = bpad / 32;
+  const size_t shard_elems = (size_t)b * Hkv * D;
+  const size_t slot_bytes = round_up((size_t)Hkv * (bpad / kKeyTile) * bwd_kblock_bytes(D), 256);
+  const size_t items_bytes = round_up((size_t)Hq * npb * bwd_item_bytes(D), 256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const __bf16* kb = static_cast<const __bf16*>(k);
+  const __bf16* vb = static_cast<const __bf16*>(v);
+
+  BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.out = static_cast<const __bf16*>(out);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.dq = dq;
+  a.b = b;
+  a.bpad = bpad;
+  a.npb = npb;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.dq_wgs_per_head = (G * npb + bwd_dq_waves() - 1) / bwd_dq_waves();
+  a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  a.scale = (float)(1.0 / std::sqrt((double)D));
+
+  auto hop = [&](int r, char* slot, hipStream_t s) -> hipError_t {
+    return launch_bwd_pack(kb + (size_t)r * shard_elems, vb + (size_t)r * shard_elems, slot, b, bpad, Hkv, D, s);
+  };
+  auto init = [&](char* extra, hipStream_t s) -> hipError_t {
+    BwdArgs x = a;
+    x.items = extra;
+    return launch_bwd_prep(x, D, s);
+  };
+  auto step = [&](char* slot, char* extra, int, int r, const BlockMask& mk, bool carry_in, bool,
+                  hipStream_t s) -> hipError_t {
+    BwdArgs x = a;
+    x.items = extra;
+    x.kslot = slot;
+    x.k = kb + (size_t)r * shard_elems;
+    x.v = vb + (size_t)r * shard_elems;
+    x.dk = dk + (size_t)r * shard_elems;
+    x.dv = dv + (size_t)r * shard_elems;
+    x.shift = mk.shift;
+    x.kend = mk.kend;
+    x.qbeg = mk.qbeg;
+    x.dq_accumulate = carry_in;
+    return launch_bwd_step(x, D, s);
+  };
+  return run_ring(P, rank, b, causal, layout, slot_bytes, items_bytes, st, hop, step, init, 3);
 }
 
 int ringattn_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows, int Hq, int d_h,
@@ -475,8 +537,8 @@ int ringattn_timing_enable(int enable) {
 }
 
 int ringattn_timing_collect(double* step_ms, int64_t* step_launches, double* merge_ms, int64_t* merge_launches) {
-  double sums[3] = {0.0, 0.0, 0.0};
-  int64_t counts[3] = {0, 0, 0};
+  double sums[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t counts[4] = {0, 0, 0, 0};
   const int status = collect_timing(0x3, sums, counts);
   if (step_ms) *step_ms = sums[0];
   if (step_launches) *step_launches = counts[0];
@@ -485,9 +547,18 @@ int ringattn_timing_collect(double* step_ms, int64_t* step_launches, double* mer
   return status;
 }
 
+int ringattn_timing_collect_backward(double* step_ms, int64_t* step_launches) {
+  double sums[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t counts[4] = {0, 0, 0, 0};
+  const int status = collect_timing(0x8, sums, counts);
+  if (step_ms) *step_ms = sums[3];
+  if (step_launches) *step_launches = counts[3];
+  return status;
+}
+
 int ringattn_timing_collect_decode(double* decode_ms, int64_t* decode_calls) {
-  double sums[3] = {0.0, 0.0, 0.0};
-  int64_t counts[3] = {0, 0, 0};
+  double sums[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t counts[4] = {0, 0, 0, 0};
   const int status = collect_timing(0x4, sums, counts);
   if (decode_ms) *decode_ms = sums[2];
   if (decode_calls) *decode_calls = counts[2];

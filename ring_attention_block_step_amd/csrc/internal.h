@@ -74,6 +74,35 @@ struct StepF32Args {
   float scale;       // 1 / sqrt(D)
 };
 
+// Backward ring step (dQ of the rank's rows, dK / dV contributions to the
+// visiting block).
+struct BwdArgs {
+  const __bf16* q;      // [b, Hq, D] the rank's query rows
+  const __bf16* out;    // [b, Hq, D] O saved by the forward
+  const __bf16* dout;   // [b, Hq, D] upstream gradient dL/dO
+  const float* lse;     // [Hq, b] LSE saved by the forward (natural log)
+  const __bf16* k;      // [b, Hkv, D] visiting shard's keys (raw layout)
+  const __bf16* v;      // [b, Hkv, D] visiting shard's values
+  const void* kslot;    // visiting shard packed for the dQ kernel: [Hkv][bpad/64] key blocks
+  void* items;          // [Hq][npb] query item blocks (written by the preparation kernel)
+  float* dq;            // [b, Hq, D] dL/dQ of the rank's rows
+  float* dk;            // [b, Hkv, D] visiting shard's dL/dK (accumulated)
+  float* dv;            // [b, Hkv, D] visiting shard's dL/dV (accumulated)
+  int b, bpad, npb, Hq, Hkv, G;   // npb: 32-row query items per head
+  int shift, kend, qbeg;          // block mask (BlockMask)
+  int dq_wgs_per_head;            // ceil(G * npb / bwd_dq_waves())
+  int dq_accumulate;              // add into dq (later visits) instead of writing it
+  float sl2;                      // log2(e) / sqrt(D)
+  float scale;                    // 1 / sqrt(D)
+};
+size_t bwd_item_bytes(int D);
+size_t bwd_kblock_bytes(int D);
+int bwd_dq_waves();
+hipError_t launch_bwd_prep(const BwdArgs& a, int D, hipStream_t st);
+hipError_t launch_bwd_pack(const __bf16* k_shard, const __bf16* v_shard, void* slot, int b, int bpad, int Hkv, int D,
+                           hipStream_t st);
+hipError_t launch_bwd_step(const BwdArgs& a, int D, hipStream_t st);
+
 // Pass-Q decode: keys per workgroup of the chunk kernel.
 constexpr int kDecodeChunk = 256;
 

@@ -1,0 +1,143 @@
+"""GPU parity of the backward ring (ringattn_backward) against the fp64 oracle.
+
+Inputs are seeded and synthetic: Q, K, V and the upstream gradient dO in
+bf16; the forward's O and LSE come from the oracle (rounded to bf16 and
+fp32), and both sides read the same rounded values.  Compared: dQ of the
+rank's rows, and the rank's contributions to every shard's dK and dV.
+
+Bound.  The kernels read bf16 inputs and round P and dS to bf16 only as MFMA
+operands, accumulating in fp32.  A bf16 rounding moves a value by at most half
+an ulp, 2^-8 of it, so each gradient entry, a sum of products with one rounded
+factor, is off by at most 2^-8 of the sum of its terms' magnitudes; with few
+terms (a row or key that sees few partners) nothing averages out.  The bound:
+mean-abs error <= 2^-8 of the tensor's mean magnitude, and max-abs error
+<= 1e-2 (about 2.5 half-ulps) of its largest magnitude.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_attention_block_step_amd as ra
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+REL_MAX = 1e-2
+REL_MEAN = 2.0 ** -8
+
+
+def _inputs(N, P, Hq, Hkv, d, seed, k_scale=1.0):
+    k = wl.token_range(seed, "k", 0, N, Hkv, d, "normal", k_scale, torch.bfloat16)
+    v = wl.token_range(seed, "v", 0, N, Hkv, d, "normal", 1.0, torch.bfloat16)
+    q = wl.token_range(seed, "q", 0, N, Hq, d, "normal", 1.0, torch.bfloat16)
+    do = wl.token_range(seed, "do", 0, N, Hq, d, "normal", 1.0, torch.bfloat16)
+    return q, k, v, do
+
+
+def _stats(got, want):
+    err = np.abs(got - want)
+    return {"max_abs": float(err.max()), "max_ref": float(np.abs(want).max()),
+            "mean_abs": float(err.mean()), "mean_ref": float(np.abs(want).mean())}
+
+
+def _check(name, got, want, label):
+    s = _stats(got, want)
+    print(f"[gpu] backward {label} {name}: {s}", flush=True)
+    assert s["max_abs"] <= REL_MAX * s["max_ref"] + 1e-6, (label, name, s)
+    assert s["mean_abs"] <= REL_MEAN * s["mean_ref"] + 1e-7, (label, name, s)
+
+
+def _run_rank(q, k, v, do, N, P, u, layout, causal, Hq, Hkv, d, dk=None, dv=None):
+    """Oracle forward for rank u (rounded), GPU backward and oracle backward."""
+    b = N // P
+    tq = oracle.shard_positions(layout, u, P, b)
+    q64, k64, v64, do64 = (t.double().numpy() for t in (q, k, v, do))
+    o, lse = oracle.ring_forward(q64[tq], u, k64, v64, P, layout, causal)
+    o16 = torch.tensor(o).to(torch.bfloat16)
+    lse32 = torch.tensor(lse).to(torch.float32)
+    kp = ra.pack_shards(k, P, layout).cuda()
+    vp = ra.pack_shards(v, P, layout).cuda()
+    gq, gk, gv = ra.backward(q[tq].cuda(), kp, vp, o16.cuda(), lse32.cuda(), do[tq].cuda(), P=P, rank=u,
+                             causal=causal, layout=layout, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    wq, wk, wv = oracle.ring_backward(q64[tq], u, k64, v64, o16.double().numpy(), lse32.double().numpy(),
+                                      do64[tq], P, layout, causal)
+    return (gq, gk, gv), (wq, wk, wv)
+
+
+CASES = [
+    # name, N, P, ranks, layout, causal, Hq, Hkv, d
+    ("ragged-contig-causal", 800, 4, (0, 1, 2, 3), "contiguous", True, 4, 2, 128),
+    ("striped-causal-d64", 1024, 4, (0, 3), "striped", True, 4, 2, 64),
+    ("zigzag-causal", 800, 4, (0, 1, 2, 3), "zigzag", True, 4, 2, 128),
+    ("contig-noncausal", 512, 2, (0, 1), "contiguous", False, 2, 1, 128),
+    ("p1-causal-gqa4", 333, 1, (0,), "contiguous", True, 4, 1, 128),
+    ("b1-striped", 8, 8, (0, 5), "striped", True, 2, 1, 128),
+    ("gqa8-striped-p8", 2048, 8, (2, 7), "striped", True, 8, 1, 128),
+]
+
+
+@pytest.mark.parametrize("name,N,P,ranks,layout,causal,Hq,Hkv,d", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(name, N, P, ranks, layout, causal, Hq, Hkv, d):
+    q, k, v, do = _inputs(N, P, Hq, Hkv, d, seed=N + P)
+    for u in ranks:
+        (gq, gk, gv), (wq, wk, wv) = _run_rank(q, k, v, do, N, P, u, layout, causal, Hq, Hkv, d)
+        label = f"{name} rank {u}"
+        _check("dq", gq.cpu().double().numpy(), wq, label)
+        _check("dk", gk.cpu().double().numpy(), wk, label)
+        _check("dv", gv.cpu().double().numpy(), wv, label)
+
+
+def test_backward_all_ranks_accumulate_to_dense_gradient():
+    """dK and dV accumulated over every rank's call equal the dense gradient;
+    every rank's dQ equals the dense dQ of its rows."""
+    N, P, Hq, Hkv, d, layout = 1024, 4, 4, 2, 128, "contiguous"
+    q, k, v, do = _inputs(N, P, Hq, Hkv, d, seed=99)
+    b = N // P
+    dk = torch.zeros(P, b, Hkv, d, device="cuda")
+    dv = torch.zeros(P, b, Hkv, d, device="cuda")
+    dq = np.zeros((N, Hq, d))
+    q64, k64, v64, do64 = (t.double().numpy() for t in (q, k, v, do))
+    for u in range(P):
+        (gq, _, _), _ = _run_rank(q, k, v, do, N, P, u, layout, True, Hq, Hkv, d, dk=dk, dv=dv)
+        dq[oracle.shard_positions(layout, u, P, b)] = gq.cpu().double().numpy()
+    # forward O is rounded to bf16 on the GPU side; the dense reference uses exact O
+    wq, wk, wv = oracle.backward_dense(q64, np.arange(N), k64, v64, do64, True)
+    gk = np.zeros((N, Hkv, d))
+    gv = np.zeros((N, Hkv, d))
+    for r in range(P):
+        tk = oracle.shard_positions(layout, r, P, b)
+        gk[tk] = dk[r].cpu().double().numpy()
+        gv[tk] = dv[r].cpu().double().numpy()
+    _check("dq", dq, wq, "all ranks")
+    _check("dk", gk, wk, "all ranks")
+    _check("dv", gv, wv, "all ranks")
+
+
+def test_backward_medium_all_rows():
+    """8k tokens, 8 shards of 1024 rows, GQA 8/2, every row of rank 5."""
+    N, P, Hq, Hkv, d = 8192, 8, 8, 2, 128
+    q, k, v, do = _inputs(N, P, Hq, Hkv, d, seed=123, k_scale=2.0)
+    (gq, gk, gv), (wq, wk, wv) = _run_rank(q, k, v, do, N, P, 5, "contiguous", True, Hq, Hkv, d)
+    _check("dq", gq.cpu().double().numpy(), wq, "medium rank 5")
+    _check("dk", gk.cpu().double().numpy(), wk, "medium rank 5")
+    _check("dv", gv.cpu().double().numpy(), wv, "medium rank 5")
+
+
+def test_backward_serial_and_overlapped_hops_are_bit_identical():
+    N, P, Hq, Hkv, d = 1024, 4, 4, 2, 128
+    q, k, v, do = _inputs(N, P, Hq, Hkv, d, seed=7)
+    res = []
+    for serial in (False, True):
+        ra.set_serial_hops(serial)
+        try:
+            (gq, gk, gv), _ = _run_rank(q, k, v, do, N, P, 3, "contiguous", True, Hq, Hkv, d)
+        finally:
+            ra.set_serial_hops(False)
+        res.append((gq.cpu(), gk.cpu(), gv.cpu()))
+    for a, b_ in zip(*res):
+        assert torch.equal(a, b_)
