@@ -21,7 +21,7 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code.  Private
 # staging arrays must stay in registers, never be moved into LDS.
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-disable-promote-alloca-to-lds",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]

@@ -22,10 +22,13 @@
 //
 // Software pipeline over the tiles every row of the workgroup sees in full,
 // in half tiles of 32 keys: block h issues the MFMAs of PV(h-1) and S(h+1)
-// while the VALU turns S(h) into probabilities, and the LDS reads of the next
-// block's fragments slot in between (a fixed MFMA / LDS / VALU issue pattern).
-// The loop body has no branch.  Tiles that need an element mask (the causal
-// diagonal, the ragged tail) run afterwards without the pipeline.
+// while the VALU turns S(h) into probabilities.  Each MFMA is followed by the
+// LDS read that refills the fragment register it consumed (the operand of the
+// same MFMA one block later) and by the softmax of one score, in an order the
+// compiler is held to; the pipeline waits for its own fragment reads, one
+// block's worth of reads behind.  The loop body has no branch.  Tiles that
+// need an element mask (the causal diagonal, the ragged tail) run afterwards
+// without the pipeline.
 //
 // Softmax in base 2: scores are scaled by log2(e)/sqrt(d) inside one FMA, and
 // m is kept in those units.  The fast kernel keeps one reference m per row for
@@ -37,6 +40,8 @@
 // launched after it recomputes that workgroup from the untouched input state
 // with the running maximum, raising the reference when a maximum exceeds it
 // by more than 8 (a factor 2^8) and rescaling y and z by exp2(m_old - m_new).
+#include <utility>
+
 #include "internal.h"
 
 namespace ringattn {
@@ -48,6 +53,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_t;
 
+__device__ __forceinline__ uint32_t lds_addr(const lds_t* p) { return (uint32_t)(uintptr_t)p; }
+
 constexpr float kLazy = 8.0f;
 
 constexpr float kLn2 = 0.69314718055994531f;
@@ -58,6 +65,30 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// An empty volatile statement that takes an MFMA result: it emits nothing,
+// but the optimiser may no longer sink the MFMA past the LDS reads that
+// follow it (MFMA builtins are pure and otherwise drift towards their uses,
+// which keeps old and new fragment registers live together).
+__device__ __forceinline__ void pin(const f32x16& acc) { asm volatile("" ::"v"(acc)); }
+
+// LDS fragment read of the fast pipeline, untracked by the compiler's wait
+// insertion: the pipeline waits for these reads itself (before each MFMA,
+// s_waitcnt lgkmcnt(one block's reads - 1), since its operand was read one
+// block's worth of reads earlier; a full drain after the loop).  Extra hardware-counted reads only make the
+// compiler's own waits stricter.  addr: per-lane LDS byte address; off: a
+// compile-time offset.
+template <int off>
+__device__ __forceinline__ void lds_frag(bf16x8& r, uint32_t addr) {
+  static_assert(off >= 0 && off < 65536, "ds_read offset");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off) : "memory");
+}
+// s_waitcnt lgkmcnt(n) alone (vmcnt and expcnt at their no-wait maxima).
+template <int n>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(n >= 0 && n < 16, "lgkmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (n << 8) | (3 << 14));
+}
+
 template <int D, int NT>
 struct Step {
   static constexpr int TILE = kKeyTile * D * 2;  // bytes of one key (or value) tile
@@ -66,6 +97,8 @@ struct Step {
   static constexpr int WAVES = 8 / NT;
   static constexpr int CHUNKS = TILE / 1024;     // 1 KB direct-load chunks per tile
   static constexpr int PER_WAVE = CHUNKS / WAVES;
+  static constexpr int kFragReads = 2 * DT + KS;  // LDS fragment reads per half-tile block of the fast loop
+  static_assert(kFragReads <= 16, "fragment reads per block must fit the lgkmcnt field");
   static_assert(PER_WAVE >= 1 && CHUNKS % WAVES == 0, "tile chunks must split over the waves");
 
   // Direct global -> LDS copy of one tile; each wave moves PER_WAVE chunks of
@@ -202,6 +235,71 @@ struct Step {
         for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma(vf[gg][dt], pb[nt][gg], o[nt][dt]);
   }
 
+  // One half-tile block of the fast pipeline, in a fixed issue order.  For
+  // every MFMA of the block (PV of the previous half tile, then the scores of
+  // the next one): the MFMA, the LDS read that refills the fragment register
+  // it has just consumed (the next block's operand), then the softmax of one
+  // score of the current half tile (of 16 NT / (MFMAs per block) scores).
+  // Compiler fences between the groups keep that order, so each read has a
+  // whole block to land before its MFMA and the VALU work is spread between
+  // the MFMAs.  zt collects the unrounded probabilities, pout their bf16
+  // packing in PV-operand order.
+  static __device__ __forceinline__ void fast_block(f32x16 (&o)[NT][DT], bf16x8 (&vf)[2][DT],
+                                                    const bf16x8 (&pprev)[NT][2], f32x16 (&snext)[NT],
+                                                    bf16x8 (&kf)[KS], const bf16x8 (&qf)[NT][KS], uint32_t vaddr,
+                                                    uint32_t kaddr, const f32x16 (&scur)[NT], const float (&mu)[NT],
+                                                    float (&zt)[NT], bf16x8 (&pout)[NT][2], float sl2) {
+    constexpr int NPV = 2 * DT * NT;
+    constexpr int NM = NPV + KS * NT;
+    constexpr int NE = 16 * NT;
+    static_assert(NE % NM == 0 || NM % NE == 0, "scores must spread evenly over the MFMAs");
+    float pv[NT][16];
+    // Scores [lo, hi) of group m: NE / NM per group, or one every NM / NE groups.
+    auto softmax_group = [&](int m) {
+      const int lo = NE >= NM ? m * (NE / NM) : ((m + 1) % (NM / NE) == 0 ? (m + 1) / (NM / NE) - 1 : 0);
+      const int hi = NE >= NM ? (m + 1) * (NE / NM) : ((m + 1) % (NM / NE) == 0 ? (m + 1) / (NM / NE) : 0);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        if (e < lo || e >= hi) continue;
+        const int nt = e / 16, r = e % 16;
+        pv[nt][r] = exp2_fast(fmaf(scur[nt][r], sl2, -mu[nt]));
+        zt[nt] += pv[nt][r];
+        if (r & 1) {
+          const f32x2 pp = {pv[nt][r - 1], pv[nt][r]};
+          const bf16x2 pk = __builtin_convertvector(pp, bf16x2);
+          pout[nt][r / 8][(r % 8) - 1] = pk[0];
+          pout[nt][r / 8][r % 8] = pk[1];
+        }
+      }
+    };
+    // Group m refills the fragment its MFMA consumed; the next block's group m
+    // uses it NR reads later (NR reads per block), after s_waitcnt
+    // lgkmcnt(NR - 1).
+    auto group = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      wait_lgkm<kFragReads - 1>();
+      if constexpr (m < NPV) {
+        constexpr int gg = m / (DT * NT), dt = (m / NT) % DT, nt = m % NT;
+        o[nt][dt] = mfma(vf[gg][dt], pprev[nt][gg], o[nt][dt]);
+        pin(o[nt][dt]);
+        if constexpr (nt == NT - 1) lds_frag<(gg * 2) * D * 16 + dt * 512>(vf[gg][dt], vaddr);
+      } else {
+        constexpr int ks = (m - NPV) / NT, nt = (m - NPV) % NT;
+        if constexpr (ks == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) snext[nt][r] = 0.f;
+        }
+        snext[nt] = mfma(kf[ks], qf[nt][ks], snext[nt]);
+        pin(snext[nt]);
+        if constexpr (nt == NT - 1) lds_frag<ks * 2048>(kf[ks], kaddr);
+      }
+      softmax_group(m);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    [&]<int... ms>(std::integer_sequence<int, ms...>) { (group(std::integral_constant<int, ms>{}), ...); }
+    (std::make_integer_sequence<int, NM>{});
+  }
+
   // O^T += V^T P^T for the 32 keys of one half tile (key groups 2*half, 2*half+1).
   static __device__ __forceinline__ void pv(f32x16 (&o)[NT][DT], const lds_t* vb, int half, const bf16x8 (&pb)[NT][2],
                                             int l32, int hi) {
@@ -232,30 +330,13 @@ __device__ __forceinline__ void wait_all_and_sync() {
 // flight here only fill LDS buffers nobody reads before the next barrier.
 // The empty asm statements keep the compiler from moving memory accesses
 // across the barrier.
-template <int n>
+template <int n, int lgkm = 0>
 __device__ __forceinline__ void wait_keep_and_sync() {
-  static_assert(n >= 0 && n < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(n | (7 << 4));
+  static_assert(n >= 0 && n < 16 && lgkm >= 0 && lgkm < 16, "waitcnt immediates");
+  __builtin_amdgcn_s_waitcnt(n | (7 << 4) | (lgkm << 8));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// Issue order of one half-tile block of the fast loop: the block's 16*NT
-// MFMAs are spread evenly, each followed by three VALU/transcendental ops of
-// the softmax, with the block's 16 LDS fragment reads placed between them, so
-// a wave keeps the matrix pipe fed while its vector ALU works (left alone,
-// the scheduler bunches the MFMAs, then the reads, then the VALU).
-// Scheduling-group masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU, 0x400 TRANS.
-template <int NT>
-__device__ __forceinline__ void interleave_block() {
-#pragma unroll
-  for (int i = 0; i < 16 * NT; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i % NT == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // A probability above this (or a NaN) sends the workgroup to the exact kernel.
@@ -273,13 +354,14 @@ void step_bf16_kernel(StepBf16Args a) {
   // The exact kernel only redoes workgroups the fast kernel flagged.
   if (EXACT && a.flags[blockIdx.x] == 0) return;
 
-  // Four key buffers (tile t in t % 4) and three value buffers (t % 3):
-  // iteration t reads K(t), K(t+1), V(t) while V(t+2) and K(t+3) stream in, so
-  // every load has a whole iteration to land before it is waited for.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[7 * S::TILE];
+  // Four key buffers and four value buffers (tile t in t % 4): iteration t
+  // reads K(t), K(t+1), V(t) while V(t+2) and K(t+3) stream in, so every load
+  // has a whole iteration to land before it is waited for, and a buffer is
+  // refilled only two iterations after its last read.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[8 * S::TILE];
   lds_t* smem = (lds_t*)(smem_raw);
   auto kbuf = [smem](int t) { return smem + (t & 3) * S::TILE; };
-  auto vbuf = [smem](int t) { return smem + (4 + t % 3) * S::TILE; };
+  auto vbuf = [smem](int t) { return smem + (4 + (t & 3)) * S::TILE; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -414,44 +496,59 @@ void step_bf16_kernel(StepBf16Args a) {
   // block's fragments (each refilled right after its last MFMA use), and the
   // VALU softmax of half tile h against the fixed reference.  No branch and no
   // VALU touch the accumulators y, so the scheduler interleaves the streams.
+  float mu[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) mu[nt] = (mref[nt] == -INFINITY) ? 0.f : mref[nt];
+  // Per-lane parts of the fragment addresses (val_tile_off / key_tile_off
+  // split into a per-lane base and compile-time offsets): value tile row
+  // d = l32 (+ 32 dt: 512 B), chunk hi (+ 2 (2 half + gg): half 1 at 4 D 16 B,
+  // gg at 2 D 16 B); key tile row l32 (+ 32 half: 512 B), chunk hi (+ 2 ks:
+  // 2048 B).
+  const uint32_t vlane = (uint32_t)(hi * D * 16 + l32 * 16);
+  const uint32_t klane = (uint32_t)(hi * 1024 + l32 * 16);
+  // Settle the prologue's reads, so that no compiler-tracked LDS read is
+  // pending inside the loop (its waits would drain the untracked ones too).
+  if (F > 0) __builtin_amdgcn_s_waitcnt(0);
   for (; t < F; ++t) {
     float zt[NT];
     // Prefetches are unconditional so the loop body is one basic block; past
     // the last tile they fill a buffer no later iteration reads (V(t+2)
-    // shares its buffer with V(t-1), K(t+3) with K(t-1)).
+    // shares its buffer with V(t-2), K(t+3) with K(t-1)).
     // block A: PV(t-1, 1), S(t, 1) | V(t).0, K(t+1).0 | probabilities of S(t, 0)
     issue_v(t + 2);
-    S::pv_f(o, vf, p1);
-    S::scores_f(sb, kf, qf);
-    S::vfrags(vf, vbuf(t), 0, l32, hi);
-    S::kfrags(kf, kbuf(t + 1), 0, l32, hi);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) zt[nt] = 0.f;
-    S::probs(sa, mref, zt, pb, a.sl2);
+    S::fast_block(o, vf, p1, sb, kf, qf, lds_addr(vbuf(t)) + vlane, lds_addr(kbuf(t + 1)) + klane, sa, mu, zt, pb,
+                  a.sl2);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       ok = ok && (zt[nt] <= kSafeSum);
       zs[nt] += zt[nt];
     }
-    interleave_block<NT>();
     // block B: PV(t, 0), S(t+1, 0) | V(t).1, K(t+1).1 | probabilities of S(t, 1)
     issue_k(t + 3);
-    S::pv_f(o, vf, pb);
-    S::scores_f(sa, kf, qf);
-    S::vfrags(vf, vbuf(t), 1, l32, hi);
-    S::kfrags(kf, kbuf(t + 1), 1, l32, hi);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) zt[nt] = 0.f;
-    S::probs(sb, mref, zt, p1, a.sl2);
+    S::fast_block(o, vf, pb, sa, kf, qf, lds_addr(vbuf(t)) + vlane + 4 * D * 16, lds_addr(kbuf(t + 1)) + klane + 512,
+                  sb, mu, zt, p1, a.sl2);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       ok = ok && (zt[nt] <= kSafeSum);
       zs[nt] += zt[nt];
     }
-    interleave_block<NT>();
-    wait_keep_and_sync<2 * S::PER_WAVE>();
+    // V(t+1), K(t+2) resident for the next iteration.  The last block's
+    // fragment reads may stay in flight (fewer than one block's worth): the
+    // buffers refilled next (V(t+3), K(t+4)) were last read in iteration t-1,
+    // whose reads are all complete by then.
+    wait_keep_and_sync<2 * S::PER_WAVE, S::kFragReads - 1>();
   }
-  if (F > 0) S::pv_f(o, vf, p1);  // PV(F-1, 1)
+  if (F > 0) {
+    // The last block's fragment reads (untracked) and the last iterations'
+    // clamped prefetches may still be in flight: drain both, so vf is valid
+    // and no prefetch writes LDS after the workgroup has finished.
+    __builtin_amdgcn_s_waitcnt(0);
+    S::pv_f(o, vf, p1);  // PV(F-1, 1)
+  }
   if (!EXACT && __builtin_amdgcn_ballot_w64(!ok) && lane == 0) a.flags[blockIdx.x] = 1;
 
   // Remaining tiles, with the exact running-maximum recurrence: element masks
