@@ -25,6 +25,9 @@
 //                     fragments in registers) and runs over the block's key
 //                     tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T,
 //                     with K, V and K^T tiles staged in LDS.
+#include <climits>
+#include <utility>
+
 #include "internal.h"
 
 namespace ringattn {
@@ -227,12 +230,20 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
 
 constexpr int kDkvWaves = 4;   // 4 waves x 32 keys = 128 keys per workgroup
 
+// Software pipeline over the query items that see the workgroup's keys: in
+// iteration it the VALU turns item it's scores into P and dS while the MFMAs
+// compute the scores S, dP of item it+1; then the MFMAs of dV^T, dK^T take
+// item it.  Items rotate through four LDS buffers (items it and it+1 read,
+// it+2 landing, it+3 issued).  A wave runs alone on its SIMD (its K, V
+// fragments and dK, dV accumulators take ~300 registers), so the two streams
+// have to overlap inside the wave.
 template <int D>
 __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   using IT = Item<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[2 * IT::BYTES];
+  constexpr int NBUF = 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[NBUF * IT::BYTES];
   lds_t* smem = (lds_t*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -249,18 +260,26 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   const int pb_lo = q_lo / 32;
   const int n_items = pb_lo < a.npb ? (a.npb - pb_lo) * a.G : 0;
 
+  // Mask (see BlockMask): query row i sees this lane's key iff i >= thr and
+  // i < b; an item whose rows all reach full_from sees every key of the wave.
+  const bool kin = key < a.b && key < a.kend;
+  const int thr = !kin ? INT_MAX : (a.shift >= 0 ? max(a.qbeg, key + a.shift) : a.qbeg);
+  const int wlast = k0 + 31;
+  const int full_from =
+      (wlast < a.b && wlast < a.kend) ? (a.shift >= 0 ? max(a.qbeg, wlast + a.shift) : a.qbeg) : INT_MAX;
+
   // K and V fragments of the wave's 32 keys (B operand: key l32, d = 16ks + 8hi ..).
   bf16x8 kf[KS], vf[KS];
   {
-    const bool kin = key < a.b;
-    const size_t base = ((size_t)(kin ? key : 0) * a.Hkv + kvh) * D;
+    const bool kb = key < a.b;
+    const size_t base = ((size_t)(kb ? key : 0) * a.Hkv + kvh) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 zk, zv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) zk[e] = zv[e] = (__bf16)0.0f;
-      kf[ks] = kin ? *reinterpret_cast<const bf16x8*>(a.k + base + ks * 16 + hi * 8) : zk;
-      vf[ks] = kin ? *reinterpret_cast<const bf16x8*>(a.v + base + ks * 16 + hi * 8) : zv;
+      kf[ks] = kb ? *reinterpret_cast<const bf16x8*>(a.k + base + ks * 16 + hi * 8) : zk;
+      vf[ks] = kb ? *reinterpret_cast<const bf16x8*>(a.v + base + ks * 16 + hi * 8) : zv;
     }
   }
   f32x16 dk[DT], dv[DT];
@@ -268,71 +287,118 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.f;
+  if (n_items == 0) goto store;
+  {
+    // Item it lands in buffer it % 4.  The source index is clamped to the last
+    // item, so a prefetch past the end reads a valid block into a buffer no
+    // later iteration reads.  Chunk c of a block goes to wave c % 4, so wave 0
+    // copies one chunk more when the block has 4n+1 chunks.
+    constexpr int PW0 = (IT::CHUNKS + kDkvWaves - 1) / kDkvWaves;
+    constexpr int PW = IT::CHUNKS / kDkvWaves;
+    auto issue_item = [&](int it) {
+      const int src = min(it, n_items - 1);
+      const int pb = pb_lo + src / a.G;
+      const int hq = kvh * a.G + src % a.G;
+      load_chunks(reinterpret_cast<const unsigned char*>(a.items) + ((size_t)hq * a.npb + pb) * IT::BYTES,
+                  smem + (it % NBUF) * IT::BYTES, IT::CHUNKS, kDkvWaves, wave, lane);
+    };
+    // Wait until this wave's copies of all but the newest `k` items landed,
+    // and every LDS read is done, then barrier.
+    auto wait_items_and_sync = [&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      static_assert(k * PW0 < 16, "vmcnt immediate");
+      if (wave == 0)
+        __builtin_amdgcn_s_waitcnt((k * PW0) | (7 << 4));
+      else
+        __builtin_amdgcn_s_waitcnt((k * PW) | (7 << 4));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    auto buf = [&](int it) { return smem + (it % NBUF) * IT::BYTES; };
 
-  auto item_src = [&](int it) {
-    const int pb = pb_lo + it / a.G;
-    const int hq = kvh * a.G + it % a.G;
-    return reinterpret_cast<const unsigned char*>(a.items) + ((size_t)hq * a.npb + pb) * IT::BYTES;
-  };
-  if (n_items > 0) load_chunks(item_src(0), smem, IT::CHUNKS, kDkvWaves, wave, lane);
-  wait_all_and_sync();
-
-  for (int it = 0; it < n_items; ++it) {
-    lds_t* cur = smem + (it & 1) * IT::BYTES;
-    if (it + 1 < n_items) load_chunks(item_src(it + 1), smem + ((it + 1) & 1) * IT::BYTES, IT::CHUNKS, kDkvWaves, wave, lane);
-    const int q0 = (pb_lo + it / a.G) * 32;
-
-    // S = Q K^T and dP = dO V^T: lane holds key l32, register r query
-    // 8(r/4) + 4hi + r%4.
-    f32x16 s, dp;
+    // S = Q K^T and dP = dO V^T of an item: lane holds key l32, register r
+    // query 8(r/4) + 4hi + r%4.
+    auto scores = [&](const lds_t* b, f32x16& s, f32x16& dp) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 qa = *reinterpret_cast<lds_frag_ptr>(cur + IT::QK + rowtile_off(l32, ks * 2 + hi));
-      const bf16x8 da = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOK + rowtile_off(l32, ks * 2 + hi));
-      s = mfma(qa, kf[ks], s);
-      dp = mfma(da, vf[ks], dp);
-    }
-    // P = exp2(S log2e/sqrt(d) - lse2), dS = P (dP - D); masked entries 0.
-    typedef const __attribute__((address_space(3))) float lds_f32;
-    typedef const f32x4 __attribute__((address_space(3)))* lds_f4_ptr;
-    lds_f32* st = (lds_f32*)(cur + IT::STATS);
-    f32x16 p, ds;
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const f32x4 l2 = *(lds_f4_ptr)(st + 8 * rg + 4 * hi);
-      const f32x4 dd = *(lds_f4_ptr)(st + 32 + 8 * rg + 4 * hi);
-      const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-      const float dvv[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = rg * 4 + x;
-        const int qi = q0 + 8 * rg + 4 * hi + x;
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -lv[x]));
-        pv = allowed(a, qi, key) ? pv : 0.f;
-        p[r] = pv;
-        ds[r] = pv * (dp[r] - dvv[x]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<lds_frag_ptr>(b + IT::QK + rowtile_off(l32, ks * 2 + hi));
+        const bf16x8 da = *reinterpret_cast<lds_frag_ptr>(b + IT::DOK + rowtile_off(l32, ks * 2 + hi));
+        s = mfma(qa, kf[ks], s);
+        dp = mfma(da, vf[ks], dp);
       }
-    }
-    const bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
-    const bf16x8 db0 = pack8(ds, 0), db1 = pack8(ds, 8);
-    // dV^T += dO^T P and dK^T += Q^T dS (A: transposed tiles, row d = 32dt + l32).
+    };
+
+    issue_item(0);
+    issue_item(1);
+    issue_item(2);
+    wait_items_and_sync(std::integral_constant<int, 1>{});   // items 0, 1 resident
+    f32x16 s, dp;
+    scores(buf(0), s, dp);
+
+    for (int it = 0; it < n_items; ++it) {
+      const lds_t* cur = buf(it);
+      issue_item(it + 3);   // buffer of item it-1, whose reads ended before the last barrier
+      const int q0 = (pb_lo + it / a.G) * 32;
+
+      // P = exp2(S log2e/sqrt(d) - lse2), dS = P (dP - D) of item it.
+      typedef const __attribute__((address_space(3))) float lds_f32;
+      typedef const f32x4 __attribute__((address_space(3)))* lds_f4_ptr;
+      lds_f32* st = (lds_f32*)(cur + IT::STATS);
+      f32x16 p, ds;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int drow = dt * 32 + l32;
-      const bf16x8 o0 = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOV + coltile_off<D>(drow, 0 + hi));
-      const bf16x8 o1 = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOV + coltile_off<D>(drow, 2 + hi));
-      const bf16x8 q0f = *reinterpret_cast<lds_frag_ptr>(cur + IT::QV + coltile_off<D>(drow, 0 + hi));
-      const bf16x8 q1f = *reinterpret_cast<lds_frag_ptr>(cur + IT::QV + coltile_off<D>(drow, 2 + hi));
-      dv[dt] = mfma(o0, pb0, dv[dt]);
-      dv[dt] = mfma(o1, pb1, dv[dt]);
-      dk[dt] = mfma(q0f, db0, dk[dt]);
-      dk[dt] = mfma(q1f, db1, dk[dt]);
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 l2 = *(lds_f4_ptr)(st + 8 * rg + 4 * hi);
+        const f32x4 dd = *(lds_f4_ptr)(st + 32 + 8 * rg + 4 * hi);
+        const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+        const float dvv[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = rg * 4 + x;
+          p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -lv[x]));
+          ds[r] = p[r] * (dp[r] - dvv[x]);
+        }
+      }
+      if (q0 < full_from || q0 + 31 >= a.b) {   // wave-uniform: some pair of the item is masked
+        const int lo = thr - q0, hiq = a.b - q0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool ok = c >= lo && c < hiq;
+          p[r] = ok ? p[r] : 0.f;
+          ds[r] = ok ? ds[r] : 0.f;
+        }
+      }
+      const bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
+      const bf16x8 db0 = pack8(ds, 0), db1 = pack8(ds, 8);
+
+      // Scores of item it+1 (past the last item: a clamped copy, unused).
+      scores(buf(it + 1), s, dp);
+
+      // dV^T += dO^T P and dK^T += Q^T dS of item it (A: transposed tiles, row d = 32dt + l32).
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int drow = dt * 32 + l32;
+        const bf16x8 o0 = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOV + coltile_off<D>(drow, 0 + hi));
+        const bf16x8 o1 = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOV + coltile_off<D>(drow, 2 + hi));
+        const bf16x8 q0f = *reinterpret_cast<lds_frag_ptr>(cur + IT::QV + coltile_off<D>(drow, 0 + hi));
+        const bf16x8 q1f = *reinterpret_cast<lds_frag_ptr>(cur + IT::QV + coltile_off<D>(drow, 2 + hi));
+        dv[dt] = mfma(o0, pb0, dv[dt]);
+        dv[dt] = mfma(o1, pb1, dv[dt]);
+        dk[dt] = mfma(q0f, db0, dk[dt]);
+        dk[dt] = mfma(q1f, db1, dk[dt]);
+      }
+      // Items it+1 and it+2 resident for the next iteration (it+3 may stay in
+      // flight); every LDS read of this iteration done before item it+4 may
+      // refill buffer it.
+      wait_items_and_sync(std::integral_constant<int, 1>{});
     }
-    wait_all_and_sync();
+    __builtin_amdgcn_s_waitcnt(0);   // drain the clamped prefetches before the waves leave
   }
 
+store:
   // Add into the caller's dK_r, dV_r: lane holds key l32, register r
   // d = 32dt + 8(r/4) + 4hi + r%4 (4 consecutive d per group).
   if (key >= a.b) return;
