@@ -82,11 +82,14 @@ __device__ __forceinline__ void lds_frag(bf16x8& r, uint32_t addr) {
   static_assert(off >= 0 && off < 65536, "ds_read offset");
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off) : "memory");
 }
-// s_waitcnt lgkmcnt(n) alone (vmcnt and expcnt at their no-wait maxima).
+// s_waitcnt lgkmcnt(n), tied to the fragment register r that the next MFMA
+// reads: r is an in/out operand of the wait, so the MFMA that uses r cannot be
+// scheduled above it (a plain waitcnt builtin orders only memory operations,
+// and the MFMA, a pure register operation, could otherwise move ahead of it).
 template <int n>
-__device__ __forceinline__ void wait_lgkm() {
+__device__ __forceinline__ void wait_lgkm_for(bf16x8& r) {
   static_assert(n >= 0 && n < 16, "lgkmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (n << 8) | (3 << 14));
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(n));
 }
 
 template <int D, int NT>
@@ -277,9 +280,9 @@ struct Step {
     // lgkmcnt(NR - 1).
     auto group = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      wait_lgkm<kFragReads - 1>();
       if constexpr (m < NPV) {
         constexpr int gg = m / (DT * NT), dt = (m / NT) % DT, nt = m % NT;
+        if constexpr (nt == 0) wait_lgkm_for<kFragReads - 1>(vf[gg][dt]);
         o[nt][dt] = mfma(vf[gg][dt], pprev[nt][gg], o[nt][dt]);
         pin(o[nt][dt]);
         if constexpr (nt == NT - 1) lds_frag<(gg * 2) * D * 16 + dt * 512>(vf[gg][dt], vaddr);
@@ -289,6 +292,7 @@ struct Step {
 #pragma unroll
           for (int r = 0; r < 16; ++r) snext[nt][r] = 0.f;
         }
+        if constexpr (nt == 0) wait_lgkm_for<kFragReads - 1>(kf[ks]);
         snext[nt] = mfma(kf[ks], qf[nt][ks], snext[nt]);
         pin(snext[nt]);
         if constexpr (nt == NT - 1) lds_frag<ks * 2048>(kf[ks], kaddr);
