@@ -13,6 +13,8 @@ step.  ``roofline`` reports the step kernel against the MI355X bf16 dense MFMA
 peak, with its average launch duration measured by HIP events around every step
 kernel inside the timed region.  ``cpu_baseline`` times the fp64 oracle on the
 host cores on a bounded sample of query rows of the same workload.
+``reference_gemm`` times the vendor's dense bf16 GEMM on the same GPU (the
+practical dense-MFMA rate under sustained load, for context).
 ``merge_kernel`` and ``decode_kernel`` report the two HBM-bound kernels (the
 triple merge; the pass-Q decode partial of one resident shard) as achieved GB/s
 against 8 TB/s; ``backward`` reports the backward ring of a workload's rank as
@@ -22,6 +24,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--cpu-seconds S] [--no-cpu-baseline] [--no-merge]
                        [--no-decode] [--decode-workload NAME] [--decode-only]
                        [--no-backward] [--backward-workload NAME] [--backward-only]
+                       [--no-gemm-ref]
 """
 
 from __future__ import annotations
@@ -223,6 +226,35 @@ def measure_merge(reps: int = 10) -> dict:
             "frac": gbs / PEAK_HBM_GBS, "launches": t["merge_launches"]}
 
 
+def measure_reference_gemm(n: int = 16384, reps: int = 10) -> dict:
+    """Context for the MFMA roofline, not a step of the path: the vendor
+    library's dense bf16 GEMM (torch.matmul, which dispatches to hipBLASLt) on
+    N(0,1) operands of n x n x n, timed with events on the same GPU in the same
+    run.  Under sustained MFMA load the chip lowers its clock well below the
+    2.4 GHz of the published peak, so this is the practical dense-MFMA rate the
+    attention kernel is compared with."""
+    import torch
+
+    g = torch.Generator(device="cuda").manual_seed(11)
+    a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"op": "bf16 GEMM (torch.matmul -> hipBLASLt), fp32 accumulate", "shape": [n, n, n], "ms": ms,
+            "value": tflops, "unit": "TFLOP/s", "frac_of_peak": tflops / PEAK_BF16_TFLOPS}
+
+
 def measure_decode(name: str = "decode-31k-gqa64", reps: int = 20) -> dict:
     """Time ringattn_decode_partial on one resident shard of a decode workload
     (HIP events around the call's kernels, inside the library) and report the
@@ -337,6 +369,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true", help="skip the merge-kernel measurement")
+    ap.add_argument("--no-gemm-ref", action="store_true", help="skip the vendor bf16 GEMM reference measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-kernel measurement")
     ap.add_argument("--decode-workload", default="decode-31k-gqa64",
                     help="decode workload of the decode-kernel measurement")
@@ -437,6 +470,7 @@ def main(argv=None) -> int:
     }
 
     merge = None if args.no_merge else measure_merge()
+    gemm = None if args.no_gemm_ref else measure_reference_gemm()
     decode = None if args.no_decode else measure_decode(args.decode_workload)
     backward = None if args.no_backward else measure_backward(args.backward_workload)
 
@@ -464,6 +498,8 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity_sample": parity,
+        "reference_gemm": gemm,
+        "step_kernel_vs_reference_gemm": (achieved / gemm["value"]) if (gemm and achieved) else None,
         "merge_kernel": merge,
         "decode_kernel": decode,
         "backward": backward,

@@ -7,37 +7,48 @@
 // The work is a stream over the shard's keys with a handful of query rows
 // (G query heads per key/value head times the new tokens), so it is bound by
 // the HBM read of K and V.  Split over keys:
-//   decode_chunk_kernel    one workgroup per (256-key chunk, key/value head,
-//                          block of query rows): scores with packed bf16 dot
-//                          products, the chunk's maximum and probabilities,
-//                          and the chunk's (m, z, y) into a workspace;
-//   decode_combine_kernel  per query row, the rescale-and-add of its chunk
-//                          partials into the shard's partial triple.
-// K and V are read once each, 16 contiguous bytes per lane, D/8 lanes per key
-// row, so every wave load covers whole key rows.
+//   decode_chunk_kernel    one workgroup of 8 waves per (256-key chunk,
+//                          key/value head, block of 32 query rows); each wave
+//                          folds 32 keys on the matrix cores and the waves'
+//                          partials are combined in LDS into the chunk's
+//                          (m, z, y) in a workspace;
+//   decode_combine_kernel  per (query row, 32 d), the rescale-and-add of the
+//                          row's chunk partials into the shard's partial triple.
+// K and V move global -> LDS with direct loads, 1 KB of whole key rows per
+// wave instruction (a lane's 16 bytes land in a swizzled chunk of its row),
+// so HBM sees fully used lines and the fragment reads are conflict-free.
 #include "internal.h"
 
 namespace ringattn {
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) unsigned char lds_t;
 
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kDecWaves = kDecodeChunk / 32;   // one wave per 32 keys of the chunk
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Sum over the `lanes` (8 or 16) consecutive lanes of a DPP row segment; every
-// lane of the segment ends with the sum.
-template <int lanes>
-__device__ __forceinline__ float segment_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)); // row_half_mirror
-  if (lanes == 16)
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)); // row_mirror
-  return x;
+// Direct global -> LDS load of 16 bytes per lane (the LDS address is the
+// wave-uniform base plus 16 * lane).  Kept in a device function: the host pass
+// of a kernel template that names this builtin directly drops the kernel's stub.
+__device__ __forceinline__ void load_lds16(const unsigned char* g, lds_t* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+// Transposed LDS read: lane i of each 16-lane group receives element i % 4 of
+// the 4 x 16-bit words addressed by lanes 4j + i / 4 (j = 0..3) of its group.
+__device__ __forceinline__ s16x4 lds_read_tr16(const lds_t* l) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_t*>(l)));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -45,195 +56,233 @@ __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
 
-// bf16 pair (low, high halves of a 32-bit word) -> two floats, exactly.
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// One wave's 32-key tiles in LDS: rows are keys (2D bytes each), stored in
+// 16-byte chunks whose index is XORed with a row-dependent swizzle:
+//   key tile:   swz_k, so that the 16 consecutive rows that one quarter of a
+//               ds_read_b128 reads (the MFMA A operand, one logical chunk of
+//               16 keys) fall in 16 distinct bank groups;
+//   value tile: swz_v, so that a ds_read_b64_tr_b16 (4 consecutive keys x
+//               64 bytes for each half of the wave) covers every bank once.
+template <int D>
+struct Dec {
+  static constexpr int CPR = D / 8;       // 16-byte chunks per key row
+  static constexpr int TB = 32 * D * 2;   // bytes of one 32-key tile
+  static constexpr int NI = TB / 1024;    // 1 KB direct loads per tile
+  static constexpr int KS = D / 16;       // k-steps of the score product
+  static constexpr int DT = D / 32;       // 32-row blocks of y^T
+  static constexpr int YS = D + 4;        // row stride (floats) of the y partials in LDS
+  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
 
-template <int D, int RB>
-__global__ __launch_bounds__(256) void decode_chunk_kernel(DecodeArgs a) {
-  constexpr int LPK = D / 8;         // lanes per key row (16 bytes each)
-  constexpr int KPI = 64 / LPK;      // key rows per wave load
-  constexpr int NI = 64 / KPI;       // wave loads per wave (64 keys per wave)
-  __shared__ float sp[RB][kDecodeChunk];          // scores, then probabilities
-  __shared__ float yw[4][RB][D];                  // per-wave y partials
-  __shared__ float stat_m[RB], stat_z[RB];
+// Chunk kernel.  Wave w of the workgroup owns keys chunk*256 + 32w .. +31:
+//   S^T = K Q^T        (v_mfma_f32_32x32x16_bf16; A = key fragments from LDS,
+//                       B = the block's 32 query rows, zero past the last row);
+//   p   = exp2(S * log2(e)/sqrt(d) - m), m = the wave's row maximum, z = sum p;
+//   y^T = V^T P^T      (A = value fragments read transposed from LDS, B = p
+//                       straight from the score registers: the transposed read
+//                       takes the keys in the order the score accumulator
+//                       holds them).  p enters as a pair of bf16 terms, its
+//                       rounding and the rounding of the remainder, so y keeps
+//                       fp32 accuracy.
+// The eight partials are then rescaled to the chunk maximum and summed.
+template <int D>
+__global__ __launch_bounds__(64 * kDecWaves) void decode_chunk_kernel(DecodeArgs a) {
+  using T = Dec<D>;
+  constexpr int TILES = kDecWaves * 2 * T::TB;         // key + value tile of every wave
+  constexpr int YW = kDecWaves * 32 * T::YS * 4;       // y partials (reuses the tile bytes)
+  constexpr int BIG = TILES > YW ? TILES : YW;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[BIG + kDecWaves * 32 * 2 * 4];
+  lds_t* smem = (lds_t*)smem_raw;
 
-  const int chunk = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int row0 = blockIdx.z * RB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int kl = lane / LPK;
-  const int dc = lane % LPK;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int chunk = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int row0 = blockIdx.z * 32;
 
-  // Query fragments: 8 bf16 of d = 8*dc .. 8*dc+7 for each row of the block.
-  uint32_t qv[RB][4];
+  const int64_t kb = (int64_t)chunk * kDecodeChunk + 32 * w;
+  const int nvalid = (int)(a.n_keys - kb < 0 ? 0 : (a.n_keys - kb > 32 ? 32 : a.n_keys - kb));
+  lds_t* kt = smem + w * 2 * T::TB;
+  lds_t* vt = kt + T::TB;
+  const size_t rstride = (size_t)a.Hkv * D;
+
+  // Direct loads of the wave's key and value rows (rows past the shard end
+  // read the last key; their scores are masked).
+  if (nvalid > 0) {
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const int rho = row0 + r;
-    uint4 x = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < T::NI; ++i) {
+      const int slot = 64 * i + lane;
+      const int r = slot / T::CPR, p = slot % T::CPR;
+      const int64_t key = kb + r < a.n_keys ? kb + r : a.n_keys - 1;
+      const unsigned char* krow = reinterpret_cast<const unsigned char*>(a.k + (size_t)key * rstride + (size_t)kvh * D);
+      const unsigned char* vrow = reinterpret_cast<const unsigned char*>(a.v + (size_t)key * rstride + (size_t)kvh * D);
+      load_lds16(krow + (p ^ T::swz_k(r)) * 16, kt + i * 1024);
+      load_lds16(vrow + (p ^ T::swz_v(r)) * 16, vt + i * 1024);
+    }
+  }
+
+  // Query fragments (B operand of S^T): lane holds row row0 + l32, logical
+  // chunk 2 ks + hi (d = 16 ks + 8 hi .. +7) at k-step ks.
+  bf16x8 qf[T::KS];
+  {
+    const int rho = row0 + l32;
     if (rho < a.rows) {
       const int t = rho / a.G, hq = kvh * a.G + rho % a.G;
-      x = *reinterpret_cast<const uint4*>(a.q + ((size_t)t * a.Hq + hq) * D + dc * 8);
-    }
-    qv[r][0] = x.x; qv[r][1] = x.y; qv[r][2] = x.z; qv[r][3] = x.w;
-  }
-
-  const int64_t kbase = (int64_t)chunk * kDecodeChunk + w * 64;
-  auto kv_addr = [&](const __bf16* base, int i) {
-    return reinterpret_cast<const uint4*>(base + ((size_t)(kbase + i * KPI + kl) * a.Hkv + kvh) * D + dc * 8);
-  };
-
-  // With few rows, every K and V row of the wave is requested before any
-  // arithmetic (NI + NI 16-byte loads per lane in flight), so the chunk's
-  // 128 KB stream in at once; with 16 rows the registers go to the row block.
-  constexpr bool PRE = RB <= 8;
-  constexpr int NP = PRE ? NI : 1;
-  uint4 kpre[NP], vpre[NP];
-  if constexpr (PRE) {
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(a.q + ((size_t)t * a.Hq + hq) * D);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const bool valid = kbase + i * KPI + kl < a.n_keys;
-      kpre[i] = valid ? *kv_addr(a.k, i) : make_uint4(0, 0, 0, 0);
-    }
+      for (int ks = 0; ks < T::KS; ++ks) qf[ks] = src[2 * ks + hi];
+    } else {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const bool valid = kbase + i * KPI + kl < a.n_keys;
-      vpre[i] = valid ? *kv_addr(a.v, i) : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.0f;
     }
   }
 
-  // Scores (log2 units): 4 packed dot products per lane, summed over the key
-  // row's LPK lanes.
-  auto score_row = [&](int i, uint4 kx) {
-    const int kloc = w * 64 + i * KPI + kl;
-    const bool valid = kbase + i * KPI + kl < a.n_keys;
+  f32x16 o[T::DT];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      float acc = dot2(qv[r][0], kx.x, 0.f);
-      acc = dot2(qv[r][1], kx.y, acc);
-      acc = dot2(qv[r][2], kx.z, acc);
-      acc = dot2(qv[r][3], kx.w, acc);
-      acc = segment_sum<LPK>(acc);
-      if (dc == 0) sp[r][kloc] = valid ? acc * a.sl2 : -INFINITY;
-    }
-  };
-  if constexpr (PRE) {
+  for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) score_row(i, kpre[i]);
-  } else {
-#pragma unroll 4
-    for (int i = 0; i < NI; ++i) {
-      const bool valid = kbase + i * KPI + kl < a.n_keys;
-      score_row(i, valid ? *kv_addr(a.k, i) : make_uint4(0, 0, 0, 0));
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m = -INFINITY, z = 0.f;
+
+  if (nvalid > 0) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed in LDS
+
+    // Scores: register r of lane (l32, hi) is query row0 + l32, key 8(r/4) + 4hi + r%4.
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
+          kt + l32 * (2 * D) + (((2 * ks + hi) ^ T::swz_k(l32)) << 4));
+      s = mfma(kf, qf[ks], s);
     }
+    if (nvalid < 32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) s[r] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    m = mx == -INFINITY ? -INFINITY : mx * a.sl2;
+    const float mu = m == -INFINITY ? 0.f : m;
+
+    // Probabilities, their sum, and the two bf16 terms of each.
+    bf16x8 ph[2], pl[2];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -mu));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], a.sl2, -mu));
+      z += p0 + p1;
+      const f32x2 pp = {p0, p1};
+      const bf16x2 h2 = __builtin_convertvector(pp, bf16x2);
+      const f32x2 rem = {p0 - (float)h2[0], p1 - (float)h2[1]};
+      const bf16x2 l2 = __builtin_convertvector(rem, bf16x2);
+      ph[r >> 3][r & 7] = h2[0];
+      ph[r >> 3][(r & 7) + 1] = h2[1];
+      pl[r >> 3][r & 7] = l2[0];
+      pl[r >> 3][(r & 7) + 1] = l2[1];
+    }
+
+    // y^T += V^T P^T.  k-step kk takes the keys of registers 8kk .. 8kk+7:
+    // 16kk + 4hi + 0..3 and 16kk + 8 + 4hi + 0..3.  A 16-lane group g of the
+    // transposed read returns, in lane i, 4 consecutive keys of d = d0 + i;
+    // its source lane s addresses key k0 + s/4, d = d0 + 4 (s%4) .. +3.
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        u32x2 half[2];
+#pragma unroll
+        for (int e4 = 0; e4 < 2; ++e4) {
+          const int row = 16 * kk + 8 * e4 + 4 * hi + (sl >> 2);
+          const int d0 = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
+          const int off = row * (2 * D) + (((d0 >> 3) ^ T::swz_v(row)) << 4) + ((d0 & 7) << 1);
+          half[e4] = __builtin_bit_cast(u32x2, lds_read_tr16(vt + off));
+        }
+        const u32x4 w4 = {half[0][0], half[0][1], half[1][0], half[1][1]};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, w4);
+        o[dt] = mfma(vf, ph[kk], o[dt]);
+        o[dt] = mfma(vf, pl[kk], o[dt]);
+      }
   }
+
+  // Combine the waves' partials in LDS (the tile bytes are free once every
+  // wave has finished its products).
+  __syncthreads();
+  float* yw = reinterpret_cast<float*>(smem_raw);          // [wave][32 rows][YS]
+  float* mw = reinterpret_cast<float*>(smem_raw + BIG);    // [wave][32]
+  float* zw = mw + kDecWaves * 32;
+  const float zpair = z + __shfl_xor(z, 32);
+  if (hi == 0) {
+    mw[w * 32 + l32] = m;
+    zw[w * 32 + l32] = zpair;
+  }
+  // y^T register r of block dt is d = 32dt + 8(r/4) + 4hi + r%4.
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      *reinterpret_cast<float4*>(yw + (w * 32 + l32) * T::YS + 32 * dt + 8 * rg + 4 * hi) =
+          make_float4(o[dt][4 * rg], o[dt][4 * rg + 1], o[dt][4 * rg + 2], o[dt][4 * rg + 3]);
   __syncthreads();
 
-  // Chunk maximum, probabilities and their sum: wave w owns rows w, w+4, ...
-  // The chunk's first key is valid, so every maximum is finite.
+  const int nr = a.rows - row0 < 32 ? a.rows - row0 : 32;
+  const size_t part = ((size_t)chunk * a.Hkv + kvh) * a.rows + row0;
+  constexpr int D4 = D / 4;
+  for (int c = tid; c < nr * D4; c += 64 * kDecWaves) {
+    const int q = c / D4, d4 = c % D4;
+    float mstar = -INFINITY;
 #pragma unroll
-  for (int r = w; r < RB; r += 4) {
-    float s[kDecodeChunk / 64];
-    float mx = -INFINITY;
+    for (int v = 0; v < kDecWaves; ++v) mstar = fmaxf(mstar, mw[v * 32 + q]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float zacc = 0.f;
 #pragma unroll
-    for (int j = 0; j < kDecodeChunk / 64; ++j) {
-      s[j] = sp[r][j * 64 + lane];
-      mx = fmaxf(mx, s[j]);
+    for (int v = 0; v < kDecWaves; ++v) {
+      const float mv = mw[v * 32 + q];
+      if (mv == -INFINITY) continue;   // an empty wave (keys past the shard end)
+      const float wt = __builtin_amdgcn_exp2f(mv - mstar);
+      const float4 yv = *reinterpret_cast<const float4*>(yw + (v * 32 + q) * T::YS + 4 * d4);
+      acc.x = fmaf(wt, yv.x, acc.x);
+      acc.y = fmaf(wt, yv.y, acc.y);
+      acc.z = fmaf(wt, yv.z, acc.z);
+      acc.w = fmaf(wt, yv.w, acc.w);
+      zacc = fmaf(wt, zw[v * 32 + q], zacc);
     }
-    mx = wave_max(mx);
-    float zs = 0.f;
-#pragma unroll
-    for (int j = 0; j < kDecodeChunk / 64; ++j) {
-      const float p = __builtin_amdgcn_exp2f(s[j] - mx);
-      sp[r][j * 64 + lane] = p;
-      zs += p;
+    *reinterpret_cast<float4*>(a.ws_y + (part + q) * D + 4 * d4) = acc;
+    if (d4 == 0) {
+      a.ws_m[part + q] = mstar;
+      a.ws_z[part + q] = zacc;
     }
-    zs = wave_sum(zs);
-    if (lane == 0) {
-      stat_m[r] = mx;
-      stat_z[r] = zs;
-    }
-  }
-  __syncthreads();
-
-  // y = sum_k p_k v_k: lane accumulates d = 8*dc .. +7 of its key rows.
-  float y[RB][8];
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[r][e] = 0.f;
-  auto pv_row = [&](int i, uint4 vx) {
-    const int kloc = w * 64 + i * KPI + kl;
-    const float vf[8] = {bf_lo(vx.x), bf_hi(vx.x), bf_lo(vx.y), bf_hi(vx.y),
-                         bf_lo(vx.z), bf_hi(vx.z), bf_lo(vx.w), bf_hi(vx.w)};
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const float p = sp[r][kloc];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[r][e] = fmaf(p, vf[e], y[r][e]);
-    }
-  };
-  if constexpr (PRE) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) pv_row(i, vpre[i]);
-  } else {
-#pragma unroll 4
-    for (int i = 0; i < NI; ++i) {
-      const bool valid = kbase + i * KPI + kl < a.n_keys;
-      pv_row(i, valid ? *kv_addr(a.v, i) : make_uint4(0, 0, 0, 0));
-    }
-  }
-  // Sum over the wave's KPI key slots (lanes with the same dc).
-#pragma unroll
-  for (int o = LPK; o < 64; o <<= 1)
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[r][e] += __shfl_xor(y[r][e], o);
-  if (kl == 0) {
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) yw[w][r][dc * 8 + e] = y[r][e];
-  }
-  __syncthreads();
-
-  // Chunk partial to the workspace: [chunk][kvh][row] (m, z) and [.][D] y.
-  const size_t part = ((size_t)chunk * a.Hkv + kvh) * a.rows;
-  for (int c = tid; c < RB * D; c += 256) {
-    const int r = c / D, d = c % D;
-    if (row0 + r < a.rows)
-      a.ws_y[(part + row0 + r) * D + d] = yw[0][r][d] + yw[1][r][d] + yw[2][r][d] + yw[3][r][d];
-  }
-  if (tid < RB && row0 + tid < a.rows) {
-    a.ws_m[part + row0 + tid] = stat_m[tid];
-    a.ws_z[part + row0 + tid] = stat_z[tid];
   }
 }
 
-// One block of 256 threads per (key/value head, query row): rescale-and-add
-// of the row's chunk partials (m in log2 units) into the shard's partial
-// triple, with m converted to natural-log units.  The chunks are spread over
-// the block (a maximum pass, then a weighted-sum pass in which each thread
-// owns 4 d and every (256 / (D/4))-th chunk), then summed through LDS.  No
-// chunk (an empty shard) gives (-inf, 0, 0).
+// One block of 256 threads per (key/value head, query row, 32 d): the
+// rescale-and-add of the row's chunk partials (m in log2 units) into the
+// shard's partial triple, with m converted to natural-log units.  The chunks
+// are spread over 32 groups of 8 threads (a maximum pass over all chunks, then
+// a weighted-sum pass in which each thread owns 4 d of every 32nd chunk),
+// then summed through LDS.  No chunk (an empty shard) gives (-inf, 0, 0).
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int DL = D / 4;        // threads per chunk row (float4 each)
+  constexpr int DL = 8;            // float4 lanes per 32 d
   constexpr int CG = 256 / DL;     // chunk groups
   __shared__ float red[4];
   __shared__ float4 ysum[CG][DL];
   __shared__ float zsum[CG];
   const int kvh = blockIdx.x / a.rows;
   const int rho = blockIdx.x % a.rows;
+  const int dsl = blockIdx.y;
   const int tid = threadIdx.x;
   const int t = rho / a.G, hq = kvh * a.G + rho % a.G;
   const size_t stride = (size_t)a.Hkv * a.rows;
@@ -247,13 +296,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
   const int dq = tid % DL, cg = tid / DL;
+  const int d = 32 * dsl + 4 * dq;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float zacc = 0.f;
 #pragma unroll 4
   for (int c = cg; c < a.nchunks; c += CG) {
     const size_t pc = base + c * stride;
     const float w = __builtin_amdgcn_exp2f(a.ws_m[pc] - mx);
-    const float4 yc = *reinterpret_cast<const float4*>(a.ws_y + pc * D + dq * 4);
+    const float4 yc = *reinterpret_cast<const float4*>(a.ws_y + pc * D + d);
     acc.x = fmaf(w, yc.x, acc.x);
     acc.y = fmaf(w, yc.y, acc.y);
     acc.z = fmaf(w, yc.z, acc.z);
@@ -272,9 +322,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
       s.z += u.z;
       s.w += u.w;
     }
-    *reinterpret_cast<float4*>(a.y_out + ((size_t)t * a.Hq + hq) * D + tid * 4) = s;
+    *reinterpret_cast<float4*>(a.y_out + ((size_t)t * a.Hq + hq) * D + 32 * dsl + tid * 4) = s;
   }
-  if (tid == 0) {
+  if (tid == 0 && dsl == 0) {
     float z = 0.f;
     for (int g = 0; g < CG; ++g) z += zsum[g];
     a.m_out[(size_t)hq * a.n_q + t] = a.nchunks > 0 ? mx * kLn2 : -INFINITY;
@@ -282,28 +332,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int RB>
-void launch_chunks(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)a.nchunks, (unsigned)a.Hkv, (unsigned)((a.rows + RB - 1) / RB));
-  hipLaunchKernelGGL((decode_chunk_kernel<D, RB>), grid, dim3(256), 0, st, a);
-}
-
 template <int D>
 void launch_all(const DecodeArgs& a, hipStream_t st) {
   if (a.nchunks > 0) {
-    if (a.rows <= 4)
-      launch_chunks<D, 4>(a, st);
-    else if (a.rows <= 8)
-      launch_chunks<D, 8>(a, st);
-    else
-      launch_chunks<D, 16>(a, st);
+    const dim3 grid((unsigned)a.nchunks, (unsigned)a.Hkv, (unsigned)((a.rows + 31) / 32));
+    hipLaunchKernelGGL((decode_chunk_kernel<D>), grid, dim3(64 * kDecWaves), 0, st, a);
   }
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.Hkv * a.rows)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.Hkv * a.rows), (unsigned)(D / 32)), dim3(256), 0,
+                     st, a);
 }
 
 }  // namespace
-
-int decode_row_block(int rows) { return rows <= 4 ? 4 : rows <= 8 ? 8 : 16; }
 
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t st) {
   if (D == 128)

@@ -156,6 +156,6 @@ hipError_t launch_merge(const float* m, const float* z, const float* y, int npar
                         int Hq, int D, void* out, int out_f32, float* lse, hipStream_t st);
 // Chunk kernel (skipped when nchunks == 0), then the combine kernel.
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t st);
-int decode_row_block(int rows);
+
 
 }  // namespace ringattn

@@ -4,9 +4,11 @@ against the fp64 oracle.
 The partial triple of a shard is not unique (any common reference for m
 cancels), so the comparison is on what is: O_p = y / z and LSE_p = m + ln z
 per shard, and O, LSE after the merge.  Bound: the inputs are bf16 (exact in
-fp32) and every quantity of the decode is fp32 (scores from packed bf16 dot
-products with fp32 accumulation, fp32 probabilities, fp32 sums), so the error
-is fp32 rounding over at most 2^17 keys: O and LSE within 1e-4 absolute.  The
+fp32); the scores are bf16 products accumulated in fp32 on the matrix cores,
+the probabilities and their sums are fp32, and each probability enters the
+p*V product as two bf16 terms (its rounding and the rounding of the
+remainder, a relative error below 2^-17), so the error is fp32 rounding over
+at most 2^17 keys: O and LSE within 1e-4 absolute.  The
 merged O is written in fp32 here and in bf16 once, where the stated bf16
 bounds apply (max-abs 1e-2, mean-abs 1e-3).
 """
@@ -63,7 +65,8 @@ SHAPES = [
     # n_q, Hq, Hkv, d, n_keys, k_scale
     (1, 4, 1, 128, 1000, 1.0),     # ragged last chunk
     (3, 8, 2, 64, 777, 2.0),       # d 64, 12 rows per key/value head
-    (5, 32, 8, 128, 300, 1.0),     # 20 rows: two row blocks
+    (5, 32, 8, 128, 300, 1.0),     # 20 rows, a chunk with empty waves
+    (5, 64, 8, 128, 2000, 1.0),    # 40 rows: two row blocks of 32
     (2, 2, 2, 128, 1, 1.0),        # one key
     (1, 16, 1, 128, 4096, 3.0),    # 16 rows, wide score spread
     (4, 4, 4, 64, 256, 1.0),       # exactly one chunk
