@@ -8,15 +8,16 @@
 // (G query heads per key/value head times the new tokens), so it is bound by
 // the HBM read of K and V.  Split over keys:
 //   decode_chunk_kernel    one workgroup of 8 waves per (256-key chunk,
-//                          key/value head, block of 32 query rows); each wave
+//                          key/value head, block of 16 query rows); each wave
 //                          folds 32 keys on the matrix cores and the waves'
 //                          partials are combined in LDS into the chunk's
 //                          (m, z, y) in a workspace;
 //   decode_combine_kernel  per (query row, 32 d), the rescale-and-add of the
 //                          row's chunk partials into the shard's partial triple.
-// K and V move global -> LDS with direct loads, 1 KB of whole key rows per
-// wave instruction (a lane's 16 bytes land in a swizzled chunk of its row),
-// so HBM sees fully used lines and the fragment reads are conflict-free.
+// Each wave loads its key rows straight into the score MFMA's A operand and
+// its value rows global -> LDS with direct loads (1 KB of whole rows per wave
+// instruction, each 16 bytes landing in a swizzled chunk of its row), where
+// the p*V product reads them transposed without bank conflicts.
 #include "internal.h"
 
 namespace ringattn {
@@ -33,6 +34,7 @@ typedef __attribute__((address_space(3))) unsigned char lds_t;
 
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kDecWaves = kDecodeChunk / 32;   // one wave per 32 keys of the chunk
+constexpr int kDecRows = 16;                    // query rows per workgroup
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -51,19 +53,10 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const lds_t* l) {
       reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_t*>(l)));
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-// One wave's 32-key tiles in LDS: rows are keys (2D bytes each), stored in
-// 16-byte chunks whose index is XORed with a row-dependent swizzle:
-//   key tile:   swz_k, so that the 16 consecutive rows that one quarter of a
-//               ds_read_b128 reads (the MFMA A operand, one logical chunk of
-//               16 keys) fall in 16 distinct bank groups;
-//   value tile: swz_v, so that a ds_read_b64_tr_b16 (4 consecutive keys x
-//               64 bytes for each half of the wave) covers every bank once.
+// One wave's 32-key value tile in LDS: rows are keys (2D bytes each), stored
+// in 16-byte chunks whose index is XORed with swz_v(row), so that a
+// ds_read_b64_tr_b16 (4 consecutive keys x 64 bytes for each half of the
+// wave) covers every bank once.
 template <int D>
 struct Dec {
   static constexpr int CPR = D / 8;       // 16-byte chunks per key row
@@ -72,13 +65,15 @@ struct Dec {
   static constexpr int KS = D / 16;       // k-steps of the score product
   static constexpr int DT = D / 32;       // 32-row blocks of y^T
   static constexpr int YS = D + 4;        // row stride (floats) of the y partials in LDS
-  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-// Chunk kernel.  Wave w of the workgroup owns keys chunk*256 + 32w .. +31:
-//   S^T = K Q^T        (v_mfma_f32_32x32x16_bf16; A = key fragments from LDS,
-//                       B = the block's 32 query rows, zero past the last row);
+// Chunk kernel.  Wave w of the workgroup owns keys chunk*256 + 32w .. +31 and
+// the block's kDecRows query rows (columns kDecRows .. 31 of the products
+// are zero):
+//   S^T = K Q^T        (v_mfma_f32_32x32x16_bf16; A = the wave's key rows,
+//                       loaded straight into the A-operand registers, B = the
+//                       query rows);
 //   p   = exp2(S * log2(e)/sqrt(d) - m), m = the wave's row maximum, z = sum p;
 //   y^T = V^T P^T      (A = value fragments read transposed from LDS, B = p
 //                       straight from the score registers: the transposed read
@@ -90,10 +85,10 @@ struct Dec {
 template <int D>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_chunk_kernel(DecodeArgs a) {
   using T = Dec<D>;
-  constexpr int TILES = kDecWaves * 2 * T::TB;         // key + value tile of every wave
-  constexpr int YW = kDecWaves * 32 * T::YS * 4;       // y partials (reuses the tile bytes)
+  constexpr int TILES = kDecWaves * T::TB;                 // value tile of every wave
+  constexpr int YW = kDecWaves * kDecRows * T::YS * 4;     // y partials (reuse the tile bytes)
   constexpr int BIG = TILES > YW ? TILES : YW;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[BIG + kDecWaves * 32 * 2 * 4];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[BIG + kDecWaves * kDecRows * 2 * 4];
   lds_t* smem = (lds_t*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -103,35 +98,40 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_chunk_kernel(DecodeArgs
   const int hi = lane >> 5;
   const int chunk = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int row0 = blockIdx.z * 32;
+  const int row0 = blockIdx.z * kDecRows;
 
   const int64_t kb = (int64_t)chunk * kDecodeChunk + 32 * w;
   const int nvalid = (int)(a.n_keys - kb < 0 ? 0 : (a.n_keys - kb > 32 ? 32 : a.n_keys - kb));
-  lds_t* kt = smem + w * 2 * T::TB;
-  lds_t* vt = kt + T::TB;
+  lds_t* vt = smem + w * T::TB;
   const size_t rstride = (size_t)a.Hkv * D;
 
-  // Direct loads of the wave's key and value rows (rows past the shard end
-  // read the last key; their scores are masked).
+  // Loads (rows past the shard end read the last key; their scores are
+  // masked): the value rows direct to LDS, 1 KB of whole rows per
+  // instruction; the key rows into the score A operand, lane (l32, hi)
+  // holding key kb + l32, logical chunk 2 ks + hi (d = 16 ks + 8 hi .. +7)
+  // at k-step ks.
+  bf16x8 kf[T::KS];
   if (nvalid > 0) {
 #pragma unroll
     for (int i = 0; i < T::NI; ++i) {
       const int slot = 64 * i + lane;
       const int r = slot / T::CPR, p = slot % T::CPR;
       const int64_t key = kb + r < a.n_keys ? kb + r : a.n_keys - 1;
-      const unsigned char* krow = reinterpret_cast<const unsigned char*>(a.k + (size_t)key * rstride + (size_t)kvh * D);
       const unsigned char* vrow = reinterpret_cast<const unsigned char*>(a.v + (size_t)key * rstride + (size_t)kvh * D);
-      load_lds16(krow + (p ^ T::swz_k(r)) * 16, kt + i * 1024);
       load_lds16(vrow + (p ^ T::swz_v(r)) * 16, vt + i * 1024);
     }
+    const int64_t key = kb + l32 < a.n_keys ? kb + l32 : a.n_keys - 1;
+    const bf16x8* krow = reinterpret_cast<const bf16x8*>(a.k + (size_t)key * rstride + (size_t)kvh * D);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) kf[ks] = krow[2 * ks + hi];
   }
 
-  // Query fragments (B operand of S^T): lane holds row row0 + l32, logical
-  // chunk 2 ks + hi (d = 16 ks + 8 hi .. +7) at k-step ks.
+  // Query fragments (B operand of S^T): lane holds row row0 + l32 (zero past
+  // the block or the last row), same chunk order as the keys.
   bf16x8 qf[T::KS];
   {
     const int rho = row0 + l32;
-    if (rho < a.rows) {
+    if (l32 < kDecRows && rho < a.rows) {
       const int t = rho / a.G, hq = kvh * a.G + rho % a.G;
       const bf16x8* src = reinterpret_cast<const bf16x8*>(a.q + ((size_t)t * a.Hq + hq) * D);
 #pragma unroll
@@ -152,18 +152,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_chunk_kernel(DecodeArgs
   float m = -INFINITY, z = 0.f;
 
   if (nvalid > 0) {
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed in LDS
-
     // Scores: register r of lane (l32, hi) is query row0 + l32, key 8(r/4) + 4hi + r%4.
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
-          kt + l32 * (2 * D) + (((2 * ks + hi) ^ T::swz_k(l32)) << 4));
-      s = mfma(kf, qf[ks], s);
-    }
+    for (int ks = 0; ks < T::KS; ++ks) s = mfma(kf[ks], qf[ks], s);
     if (nvalid < 32) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -193,6 +187,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_chunk_kernel(DecodeArgs
       pl[r >> 3][(r & 7) + 1] = l2[1];
     }
 
+    // The value tile has landed (the key registers were waited for above).
+    __builtin_amdgcn_s_waitcnt(0);
+
     // y^T += V^T P^T.  k-step kk takes the keys of registers 8kk .. 8kk+7:
     // 16kk + 4hi + 0..3 and 16kk + 8 + 4hi + 0..3.  A 16-lane group g of the
     // transposed read returns, in lane i, 4 consecutive keys of d = d0 + i;
@@ -220,44 +217,46 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_chunk_kernel(DecodeArgs
   // Combine the waves' partials in LDS (the tile bytes are free once every
   // wave has finished its products).
   __syncthreads();
-  float* yw = reinterpret_cast<float*>(smem_raw);          // [wave][32 rows][YS]
-  float* mw = reinterpret_cast<float*>(smem_raw + BIG);    // [wave][32]
-  float* zw = mw + kDecWaves * 32;
+  float* yw = reinterpret_cast<float*>(smem_raw);          // [wave][kDecRows][YS]
+  float* mw = reinterpret_cast<float*>(smem_raw + BIG);    // [wave][kDecRows]
+  float* zw = mw + kDecWaves * kDecRows;
   const float zpair = z + __shfl_xor(z, 32);
-  if (hi == 0) {
-    mw[w * 32 + l32] = m;
-    zw[w * 32 + l32] = zpair;
+  if (l32 < kDecRows) {
+    if (hi == 0) {
+      mw[w * kDecRows + l32] = m;
+      zw[w * kDecRows + l32] = zpair;
+    }
+    // y^T register r of block dt is d = 32dt + 8(r/4) + 4hi + r%4.
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *reinterpret_cast<float4*>(yw + (w * kDecRows + l32) * T::YS + 32 * dt + 8 * rg + 4 * hi) =
+            make_float4(o[dt][4 * rg], o[dt][4 * rg + 1], o[dt][4 * rg + 2], o[dt][4 * rg + 3]);
   }
-  // y^T register r of block dt is d = 32dt + 8(r/4) + 4hi + r%4.
-#pragma unroll
-  for (int dt = 0; dt < T::DT; ++dt)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
-      *reinterpret_cast<float4*>(yw + (w * 32 + l32) * T::YS + 32 * dt + 8 * rg + 4 * hi) =
-          make_float4(o[dt][4 * rg], o[dt][4 * rg + 1], o[dt][4 * rg + 2], o[dt][4 * rg + 3]);
   __syncthreads();
 
-  const int nr = a.rows - row0 < 32 ? a.rows - row0 : 32;
+  const int nr = a.rows - row0 < kDecRows ? a.rows - row0 : kDecRows;
   const size_t part = ((size_t)chunk * a.Hkv + kvh) * a.rows + row0;
   constexpr int D4 = D / 4;
   for (int c = tid; c < nr * D4; c += 64 * kDecWaves) {
     const int q = c / D4, d4 = c % D4;
     float mstar = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kDecWaves; ++v) mstar = fmaxf(mstar, mw[v * 32 + q]);
+    for (int v = 0; v < kDecWaves; ++v) mstar = fmaxf(mstar, mw[v * kDecRows + q]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float zacc = 0.f;
 #pragma unroll
     for (int v = 0; v < kDecWaves; ++v) {
-      const float mv = mw[v * 32 + q];
+      const float mv = mw[v * kDecRows + q];
       if (mv == -INFINITY) continue;   // an empty wave (keys past the shard end)
       const float wt = __builtin_amdgcn_exp2f(mv - mstar);
-      const float4 yv = *reinterpret_cast<const float4*>(yw + (v * 32 + q) * T::YS + 4 * d4);
+      const float4 yv = *reinterpret_cast<const float4*>(yw + (v * kDecRows + q) * T::YS + 4 * d4);
       acc.x = fmaf(wt, yv.x, acc.x);
       acc.y = fmaf(wt, yv.y, acc.y);
       acc.z = fmaf(wt, yv.z, acc.z);
       acc.w = fmaf(wt, yv.w, acc.w);
-      zacc = fmaf(wt, zw[v * 32 + q], zacc);
+      zacc = fmaf(wt, zw[v * kDecRows + q], zacc);
     }
     *reinterpret_cast<float4*>(a.ws_y + (part + q) * D + 4 * d4) = acc;
     if (d4 == 0) {
@@ -269,17 +268,18 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_chunk_kernel(DecodeArgs
 
 // One block of 256 threads per (key/value head, query row, 32 d): the
 // rescale-and-add of the row's chunk partials (m in log2 units) into the
-// shard's partial triple, with m converted to natural-log units.  The chunks
-// are spread over 32 groups of 8 threads (a maximum pass over all chunks, then
-// a weighted-sum pass in which each thread owns 4 d of every 32nd chunk),
-// then summed through LDS.  No chunk (an empty shard) gives (-inf, 0, 0).
+// shard's partial triple, with m converted to natural-log units.  A thread
+// owns 4 d of every 32nd chunk; it issues the loads of all its chunks before
+// folding them with a running maximum, so the pass costs one memory latency.
+// The 32 chunk groups are then merged through LDS the same way.  No chunk
+// (an empty shard) gives (-inf, 0, 0).
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int DL = 8;            // float4 lanes per 32 d
   constexpr int CG = 256 / DL;     // chunk groups
-  __shared__ float red[4];
+  constexpr int NB = 8;            // chunks in flight per thread
   __shared__ float4 ysum[CG][DL];
-  __shared__ float zsum[CG];
+  __shared__ float msum[CG], zsum[CG];
   const int kvh = blockIdx.x / a.rows;
   const int rho = blockIdx.x % a.rows;
   const int dsl = blockIdx.y;
@@ -287,55 +287,71 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int t = rho / a.G, hq = kvh * a.G + rho % a.G;
   const size_t stride = (size_t)a.Hkv * a.rows;
   const size_t base = (size_t)kvh * a.rows + rho;
-
-  float mx = -INFINITY;
-  for (int c = tid; c < a.nchunks; c += 256) mx = fmaxf(mx, a.ws_m[base + c * stride]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
   const int dq = tid % DL, cg = tid / DL;
   const int d = 32 * dsl + 4 * dq;
+
+  float mr = -INFINITY, zr = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float zacc = 0.f;
-#pragma unroll 4
-  for (int c = cg; c < a.nchunks; c += CG) {
-    const size_t pc = base + c * stride;
-    const float w = __builtin_amdgcn_exp2f(a.ws_m[pc] - mx);
-    const float4 yc = *reinterpret_cast<const float4*>(a.ws_y + pc * D + d);
-    acc.x = fmaf(w, yc.x, acc.x);
-    acc.y = fmaf(w, yc.y, acc.y);
-    acc.z = fmaf(w, yc.z, acc.z);
-    acc.w = fmaf(w, yc.w, acc.w);
-    zacc = fmaf(w, a.ws_z[pc], zacc);
+  for (int c0 = cg; c0 < a.nchunks; c0 += CG * NB) {
+    float mc[NB], zc[NB];
+    float4 yc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int c = c0 + j * CG;
+      const size_t pc = base + (size_t)(c < a.nchunks ? c : 0) * stride;
+      mc[j] = c < a.nchunks ? a.ws_m[pc] : -INFINITY;
+      zc[j] = a.ws_z[pc];
+      yc[j] = *reinterpret_cast<const float4*>(a.ws_y + pc * D + d);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (mc[j] == -INFINITY) continue;
+      const float mn = fmaxf(mr, mc[j]);
+      const float so = __builtin_amdgcn_exp2f(mr - mn);   // 0 while nothing is folded in
+      const float sc = __builtin_amdgcn_exp2f(mc[j] - mn);
+      acc.x = fmaf(sc, yc[j].x, acc.x * so);
+      acc.y = fmaf(sc, yc[j].y, acc.y * so);
+      acc.z = fmaf(sc, yc[j].z, acc.z * so);
+      acc.w = fmaf(sc, yc[j].w, acc.w * so);
+      zr = fmaf(sc, zc[j], zr * so);
+      mr = mn;
+    }
   }
   ysum[cg][dq] = acc;
-  if (dq == 0) zsum[cg] = zacc;
+  if (dq == 0) {
+    msum[cg] = mr;
+    zsum[cg] = zr;
+  }
   __syncthreads();
   if (tid < DL) {
-    float4 s = ysum[0][tid];
-    for (int g = 1; g < CG; ++g) {
-      const float4 u = ysum[g][tid];
-      s.x += u.x;
-      s.y += u.y;
-      s.z += u.z;
-      s.w += u.w;
+    float mx = -INFINITY;
+    for (int g = 0; g < CG; ++g) mx = fmaxf(mx, msum[g]);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    float z = 0.f;
+    if (mx != -INFINITY) {
+      for (int g = 0; g < CG; ++g) {
+        if (msum[g] == -INFINITY) continue;
+        const float wg = __builtin_amdgcn_exp2f(msum[g] - mx);
+        const float4 u = ysum[g][tid];
+        s.x = fmaf(wg, u.x, s.x);
+        s.y = fmaf(wg, u.y, s.y);
+        s.z = fmaf(wg, u.z, s.z);
+        s.w = fmaf(wg, u.w, s.w);
+        z = fmaf(wg, zsum[g], z);
+      }
     }
     *reinterpret_cast<float4*>(a.y_out + ((size_t)t * a.Hq + hq) * D + 32 * dsl + tid * 4) = s;
-  }
-  if (tid == 0 && dsl == 0) {
-    float z = 0.f;
-    for (int g = 0; g < CG; ++g) z += zsum[g];
-    a.m_out[(size_t)hq * a.n_q + t] = a.nchunks > 0 ? mx * kLn2 : -INFINITY;
-    a.z_out[(size_t)hq * a.n_q + t] = z;
+    if (tid == 0 && dsl == 0) {
+      a.m_out[(size_t)hq * a.n_q + t] = mx == -INFINITY ? -INFINITY : mx * kLn2;
+      a.z_out[(size_t)hq * a.n_q + t] = z;
+    }
   }
 }
 
 template <int D>
 void launch_all(const DecodeArgs& a, hipStream_t st) {
   if (a.nchunks > 0) {
-    const dim3 grid((unsigned)a.nchunks, (unsigned)a.Hkv, (unsigned)((a.rows + 31) / 32));
+    const dim3 grid((unsigned)a.nchunks, (unsigned)a.Hkv, (unsigned)((a.rows + kDecRows - 1) / kDecRows));
     hipLaunchKernelGGL((decode_chunk_kernel<D>), grid, dim3(64 * kDecWaves), 0, st, a);
   }
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.Hkv * a.rows), (unsigned)(D / 32)), dim3(256), 0,

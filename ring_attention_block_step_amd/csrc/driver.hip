@@ -482,7 +482,7 @@ int ringattn_decode_partial(const void* q, const void* k, const void* v, int n_q
   if (d_h != 64 && d_h != 128) return fail(RINGATTN_EUNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
   const int64_t rows = (int64_t)(Hq / Hkv) * n_q;
   const int64_t nchunks = (n_keys + kDecodeChunk - 1) / kDecodeChunk;
-  if (rows * Hkv > ((int64_t)1 << 30) || nchunks > ((int64_t)1 << 30) || (rows + 31) / 32 > 65535)
+  if (rows * Hkv > ((int64_t)1 << 30) || nchunks > ((int64_t)1 << 30) || (rows + 15) / 16 > 65535)
     return fail(RINGATTN_EUNSUPPORTED, "decode shape too large (n_q=%d, Hq=%d, n_keys=%lld)", n_q, Hq,
                 (long long)n_keys);
   hipStream_t st = static_cast<hipStream_t>(stream);
