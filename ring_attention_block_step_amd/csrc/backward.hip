@@ -229,6 +229,7 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
 // ---------------------------------------------------------------------------
 
 constexpr int kDkvWaves = 4;   // 4 waves x 32 keys = 128 keys per workgroup
+constexpr int kXcds = 8;       // accelerator complex dies; workgroup L is dispatched to die L % 8
 
 // Software pipeline over the query items that see the workgroup's keys: in
 // iteration it the VALU turns item it's scores into P and dS while the MFMAs
@@ -248,8 +249,15 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int kvh = blockIdx.y;
-  const int wk0 = blockIdx.x * (32 * kDkvWaves);
+  // XCD-aware placement: workgroup L runs on XCD L % kXcds, and consecutive
+  // (key/value head, key block) pairs go to one XCD, so the workgroups that
+  // stream the same head's query items share that XCD's L2.
+  const int nkb = (a.b + 32 * kDkvWaves - 1) / (32 * kDkvWaves);
+  const int per_xcd = (nkb * a.Hkv + kXcds - 1) / kXcds;
+  const int idx = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (idx >= nkb * a.Hkv) return;
+  const int kvh = idx / nkb;
+  const int wk0 = (idx % nkb) * (32 * kDkvWaves);
   const int k0 = wk0 + wave * 32;
   const int key = k0 + l32;
 
@@ -574,7 +582,8 @@ hipError_t launch_bwd_pack(const __bf16* k_shard, const __bf16* v_shard, void* s
 }
 
 hipError_t launch_bwd_step(const BwdArgs& a, int D, hipStream_t st) {
-  const dim3 gkv((unsigned)((a.b + 32 * kDkvWaves - 1) / (32 * kDkvWaves)), (unsigned)a.Hkv);
+  const int nkb = (a.b + 32 * kDkvWaves - 1) / (32 * kDkvWaves);
+  const dim3 gkv((unsigned)((nkb * a.Hkv + kXcds - 1) / kXcds * kXcds));
   const dim3 gq((unsigned)(a.dq_wgs_per_head * a.Hkv));
   if (D == 128) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gkv, dim3(64 * kDkvWaves), 0, st, a);
