@@ -53,21 +53,25 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 __host__ __device__ inline int perm16(int kappa) { return (kappa & 3) | ((kappa & 4) << 1) | ((kappa & 8) >> 1); }
 
 // Query item block (32 rows of one query head), copied to LDS verbatim:
-//   [Q  row-major 32 x D][dO row-major][Q^T D x 32][dO^T D x 32][stats 1 KB]
-// row-major: 16-byte chunk c (d = 8c .. 8c+7) of row j at c*512 + j*16;
-// transposed: row d, chunk c (queries 8c .. 8c+7 in storage order, query
-// 16*(c/2) + perm16(8*(c%2) + e) at element e) at c*D*16 + d*16;
-// stats: lse2[32] (LSE * log2 e; +inf for a row that saw no key), then D[32].
+//   [Q 32 x D][dO 32 x D][stats: lse2[32] (LSE * log2 e; +inf for a row that
+//   saw no key), then D[32]], padded to whole KB.
+// Q and dO are row-major (row = query, 2D bytes), each 16-byte chunk at an
+// XOR-swizzled position, so that both reads of the dK/dV kernel are free of
+// bank conflicts: the MFMA A-operand read (16 lanes = 16 consecutive rows, one
+// logical chunk) and the transposed read ds_read_b64_tr_b16 (4 consecutive
+// rows x 64 bytes per half wave) that gives the Q^T, dO^T operands.
 template <int D>
 struct Item {
   static constexpr int TILE = 32 * D * 2;
-  static constexpr int QK = 0, DOK = TILE, QV = 2 * TILE, DOV = 3 * TILE, STATS = 4 * TILE;
-  static constexpr int BYTES = 4 * TILE + 1024;
+  static constexpr int QK = 0, DOK = TILE, STATS = 2 * TILE;
+  static constexpr int BYTES = (2 * TILE + 256 + 1023) / 1024 * 1024;
   static constexpr int CHUNKS = BYTES / 1024;
+  static __host__ __device__ __forceinline__ int swz(int r) {
+    return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+  }
+  // Byte offset of logical 16-byte chunk c (d = 8c .. 8c+7) of row r.
+  static __host__ __device__ __forceinline__ int off(int r, int c) { return r * (2 * D) + ((c ^ swz(r)) << 4); }
 };
-__host__ __device__ inline int rowtile_off(int row, int chunk) { return chunk * 512 + row * 16; }
-template <int D>
-__host__ __device__ inline int coltile_off(int drow, int chunk) { return chunk * (D * 16) + drow * 16; }
 
 // Key tile block of the dQ kernel's slot (64 keys of one key/value head):
 //   [K row-major (key_tile_off)][V row-major (key_tile_off)][K^T (val_tile_off)]
@@ -97,8 +101,6 @@ __device__ __forceinline__ bool allowed(const BwdArgs& a, int i, int j) {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;
-  constexpr int VS = D + 8;               // LDS pitch (elements) of the staging rows
-  __shared__ uint16_t sq[32 * VS], sd[32 * VS];
   const int pb = blockIdx.x, hq = blockIdx.y;
   const int q0 = pb * 32;
   unsigned char* blk = reinterpret_cast<unsigned char*>(a.items) + ((size_t)hq * a.npb + pb) * Item<D>::BYTES;
@@ -114,12 +116,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
       qv = *reinterpret_cast<const uint4*>(q + src);
       dv = *reinterpret_cast<const uint4*>(dout + src);
     }
-    *reinterpret_cast<uint4*>(blk + Item<D>::QK + rowtile_off(row, cc)) = qv;
-    *reinterpret_cast<uint4*>(blk + Item<D>::DOK + rowtile_off(row, cc)) = dv;
-    *reinterpret_cast<uint2*>(sq + row * VS + cc * 8) = make_uint2(qv.x, qv.y);
-    *reinterpret_cast<uint2*>(sq + row * VS + cc * 8 + 4) = make_uint2(qv.z, qv.w);
-    *reinterpret_cast<uint2*>(sd + row * VS + cc * 8) = make_uint2(dv.x, dv.y);
-    *reinterpret_cast<uint2*>(sd + row * VS + cc * 8 + 4) = make_uint2(dv.z, dv.w);
+    *reinterpret_cast<uint4*>(blk + Item<D>::QK + Item<D>::off(row, cc)) = qv;
+    *reinterpret_cast<uint4*>(blk + Item<D>::DOK + Item<D>::off(row, cc)) = dv;
   }
   // Stats: D = rowsum(dO * O) in fp32 from the bf16 values, LSE in log2 units.
   if (threadIdx.x < 32) {
@@ -136,27 +134,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     float* st = reinterpret_cast<float*>(blk + Item<D>::STATS);
     st[row] = l2;
     st[32 + row] = dsum;
-  }
-  __syncthreads();
-  // Transposed tiles: row d, chunk c holds queries in storage order.
-  for (int c = threadIdx.x; c < D * 4; c += 256) {
-    const int d = c / 4, ch = c % 4;
-    uint32_t wq[4], wd[4];
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      uint32_t pq[2], pd[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int kappa = 8 * (ch % 2) + e + x;
-        const int row = 16 * (ch / 2) + perm16(kappa);
-        pq[x] = sq[row * VS + d];
-        pd[x] = sd[row * VS + d];
-      }
-      wq[e / 2] = pq[0] | (pq[1] << 16);
-      wd[e / 2] = pd[0] | (pd[1] << 16);
-    }
-    *reinterpret_cast<uint4*>(blk + Item<D>::QV + coltile_off<D>(d, ch)) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
-    *reinterpret_cast<uint4*>(blk + Item<D>::DOV + coltile_off<D>(d, ch)) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
 }
 
@@ -228,37 +205,94 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
 // dK, dV of the visiting block.
 // ---------------------------------------------------------------------------
 
-constexpr int kDkvWaves = 4;   // 4 waves x 32 keys = 128 keys per workgroup
+constexpr int kDkvPairs = 4;  // 4 pairs of waves x 32 keys = 128 keys per workgroup
+constexpr int kDkvWaves = 2 * kDkvPairs;
 constexpr int kXcds = 8;       // accelerator complex dies; workgroup L is dispatched to die L % 8
+constexpr int kDkvBufs = 6;    // LDS ring of query items: it-1 .. it+4 during iteration it
+constexpr int kXchBytes = 4096;  // packed P and dS of one item for one wave pair
 
-// Software pipeline over the query items that see the workgroup's keys: in
-// iteration it the VALU turns item it's scores into P and dS while the MFMAs
-// compute the scores S, dP of item it+1; then the MFMAs of dV^T, dK^T take
-// item it.  Items rotate through four LDS buffers (items it and it+1 read,
-// it+2 landing, it+3 issued).  A wave runs alone on its SIMD (its K, V
-// fragments and dK, dV accumulators take ~300 registers), so the two streams
-// have to overlap inside the wave.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed LDS read: lane i of each 16-lane group receives element i % 4 of
+// the 4 x 16-bit words addressed by lanes 4j + i / 4 (j = 0..3) of its group.
+__device__ __forceinline__ u32x2 lds_read_tr16(const lds_t* l) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_t*>(l))));
+}
+__device__ __forceinline__ void load_lds16(const unsigned char* g, lds_t* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+// Fragment reads of an item tile (IT::QK or IT::DOK) held in LDS.
+template <int D>
+struct ItemFrag {
+  using IT = Item<D>;
+  // Row fragment, the A operand of S = Q K^T or dP = dO V^T: lane (l32, hi)
+  // holds row l32, d = 16 ks + 8 hi .. +7.
+  static __device__ __forceinline__ bf16x8 row(const lds_t* tile, int ks, int l32, int hi) {
+    return *reinterpret_cast<lds_frag_ptr>(tile + IT::off(l32, 2 * ks + hi));
+  }
+  // Transposed fragment, the A operand of dV^T += dO^T P or dK^T += Q^T dS:
+  // lane (l32, hi) holds d = 32 dt + l32 of the 8 queries that B element e
+  // stands for at k-step kk, 16 kk + 8 (e/4) + 4 hi + e%4 (the order in which
+  // the score accumulator hands its rows to the lane).  Two transposed reads
+  // of 4 queries each; source lane (g, sl) addresses query row
+  // 16 kk + 8 e4 + 4 hi + sl/4, d = 32 dt + 16 (g%2) + 4 (sl%4) .. +3.
+  static __device__ __forceinline__ bf16x8 tr(const lds_t* tile, int dt, int kk, int lane) {
+    const int g = lane >> 4, sl = lane & 15, hi = lane >> 5;
+    u32x2 h[2];
+#pragma unroll
+    for (int e4 = 0; e4 < 2; ++e4) {
+      const int row = 16 * kk + 8 * e4 + 4 * hi + (sl >> 2);
+      const int d0 = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
+      h[e4] = lds_read_tr16(tile + IT::off(row, d0 >> 3) + ((d0 & 7) << 1));
+    }
+    const u32x4 w = {h[0][0], h[0][1], h[1][0], h[1][1]};
+    return __builtin_bit_cast(bf16x8, w);
+  }
+};
+
+// dK and dV of the visiting block.  The workgroup owns 128 keys; each 32 of
+// them belong to a pair of waves that share a SIMD:
+//   the score wave   (K, V fragments in registers) forms S = Q K^T and
+//                    dP = dO V^T of an item, P = exp2(S log2e/sqrt(d) - lse2)
+//                    and dS = P (dP - D) with the element mask where the item
+//                    straddles the causal diagonal or the shard end, and
+//                    leaves P and dS, packed to bf16 in its register order,
+//                    in LDS;
+//   the gradient wave (dK^T, dV^T accumulators) takes them one item later and
+//                    folds dV^T += dO^T P and dK^T += Q^T dS, with the
+//                    transposed operands read from the same item tiles.
+// Two waves per SIMD, each within 256 registers, so the matrix cores of one
+// overlap the vector work of the other.  Items rotate through a ring of
+// kDkvBufs LDS buffers: in iteration it the score waves read item it, the
+// gradient waves item it-1, and items it+1 .. it+4 are resident or in flight.
 template <int D>
 __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   using IT = Item<D>;
-  constexpr int NBUF = 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[NBUF * IT::BYTES];
+  using F = ItemFrag<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kDkvBufs * IT::BYTES + 2 * kDkvPairs * kXchBytes];
   lds_t* smem = (lds_t*)smem_raw;
+  lds_t* xch = smem + kDkvBufs * IT::BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
+  const bool scorer = wave < kDkvPairs;
+  const int pair = scorer ? wave : wave - kDkvPairs;
   // XCD-aware placement: workgroup L runs on XCD L % kXcds, and consecutive
   // (key/value head, key block) pairs go to one XCD, so the workgroups that
   // stream the same head's query items share that XCD's L2.
-  const int nkb = (a.b + 32 * kDkvWaves - 1) / (32 * kDkvWaves);
+  const int nkb = (a.b + 32 * kDkvPairs - 1) / (32 * kDkvPairs);
   const int per_xcd = (nkb * a.Hkv + kXcds - 1) / kXcds;
   const int idx = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
   if (idx >= nkb * a.Hkv) return;
   const int kvh = idx / nkb;
-  const int wk0 = (idx % nkb) * (32 * kDkvWaves);
-  const int k0 = wk0 + wave * 32;
+  const int wk0 = (idx % nkb) * (32 * kDkvPairs);
+  const int k0 = wk0 + pair * 32;
   const int key = k0 + l32;
 
   // Query rows that may see any key of the workgroup: from q_lo on.
@@ -269,106 +303,105 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   const int n_items = pb_lo < a.npb ? (a.npb - pb_lo) * a.G : 0;
 
   // Mask (see BlockMask): query row i sees this lane's key iff i >= thr and
-  // i < b; an item whose rows all reach full_from sees every key of the wave.
+  // i < b; an item whose rows all reach full_from sees every key of the pair.
   const bool kin = key < a.b && key < a.kend;
   const int thr = !kin ? INT_MAX : (a.shift >= 0 ? max(a.qbeg, key + a.shift) : a.qbeg);
-  const int wlast = k0 + 31;
+  const int plast = k0 + 31;
   const int full_from =
-      (wlast < a.b && wlast < a.kend) ? (a.shift >= 0 ? max(a.qbeg, wlast + a.shift) : a.qbeg) : INT_MAX;
+      (plast < a.b && plast < a.kend) ? (a.shift >= 0 ? max(a.qbeg, plast + a.shift) : a.qbeg) : INT_MAX;
 
-  // K and V fragments of the wave's 32 keys (B operand: key l32, d = 16ks + 8hi ..).
-  bf16x8 kf[KS], vf[KS];
-  {
-    const bool kb = key < a.b;
-    const size_t base = ((size_t)(kb ? key : 0) * a.Hkv + kvh) * D;
+  // Item it lands in buffer it % kDkvBufs.  The source index is clamped to
+  // the last item, so a prefetch past the end reads a valid block into a
+  // buffer no later iteration reads.  Chunk c of a block goes to wave
+  // c % kDkvWaves, so the first CHUNKS % kDkvWaves waves copy one more.
+  constexpr int PWX = (IT::CHUNKS + kDkvWaves - 1) / kDkvWaves;
+  constexpr int PW = IT::CHUNKS / kDkvWaves;
+  constexpr int NX = IT::CHUNKS - PW * kDkvWaves;   // waves that copy PWX chunks
+  constexpr int AHEAD = 3;                          // items left in flight at each barrier
+  static_assert(AHEAD * PWX < 16, "vmcnt immediate");
+  auto buf = [&](int it) { return smem + (it % kDkvBufs) * IT::BYTES; };
+  auto issue_item = [&](int it) {
+    const int src = min(it, n_items - 1);
+    const int pb = pb_lo + src / a.G;
+    const int hq = kvh * a.G + src % a.G;
+    const unsigned char* g = reinterpret_cast<const unsigned char*>(a.items) + ((size_t)hq * a.npb + pb) * IT::BYTES;
+    lds_t* l = buf(it);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 zk, zv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) zk[e] = zv[e] = (__bf16)0.0f;
-      kf[ks] = kb ? *reinterpret_cast<const bf16x8*>(a.k + base + ks * 16 + hi * 8) : zk;
-      vf[ks] = kb ? *reinterpret_cast<const bf16x8*>(a.v + base + ks * 16 + hi * 8) : zv;
+    for (int i = 0; i < PWX; ++i) {
+      const int c = wave + kDkvWaves * i;
+      if (i < PW || c < IT::CHUNKS) load_lds16(g + c * 1024 + lane * 16, l + c * 1024);
     }
-  }
-  f32x16 dk[DT], dv[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.f;
-  if (n_items == 0) goto store;
-  {
-    // Item it lands in buffer it % 4.  The source index is clamped to the last
-    // item, so a prefetch past the end reads a valid block into a buffer no
-    // later iteration reads.  Chunk c of a block goes to wave c % 4, so wave 0
-    // copies one chunk more when the block has 4n+1 chunks.
-    constexpr int PW0 = (IT::CHUNKS + kDkvWaves - 1) / kDkvWaves;
-    constexpr int PW = IT::CHUNKS / kDkvWaves;
-    auto issue_item = [&](int it) {
-      const int src = min(it, n_items - 1);
-      const int pb = pb_lo + src / a.G;
-      const int hq = kvh * a.G + src % a.G;
-      load_chunks(reinterpret_cast<const unsigned char*>(a.items) + ((size_t)hq * a.npb + pb) * IT::BYTES,
-                  smem + (it % NBUF) * IT::BYTES, IT::CHUNKS, kDkvWaves, wave, lane);
-    };
-    // Wait until this wave's copies of all but the newest `k` items landed,
-    // and every LDS read is done, then barrier.
-    auto wait_items_and_sync = [&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      static_assert(k * PW0 < 16, "vmcnt immediate");
-      if (wave == 0)
-        __builtin_amdgcn_s_waitcnt((k * PW0) | (7 << 4));
-      else
-        __builtin_amdgcn_s_waitcnt((k * PW) | (7 << 4));
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
-    auto buf = [&](int it) { return smem + (it % NBUF) * IT::BYTES; };
+  };
+  // Wait until this wave's copies of all but the newest AHEAD items landed
+  // and its LDS accesses are done, then barrier.
+  auto wait_items_and_sync = [&]() {
+    if (wave < NX)
+      __builtin_amdgcn_s_waitcnt((AHEAD * PWX) | (7 << 4));
+    else
+      __builtin_amdgcn_s_waitcnt((AHEAD * PW) | (7 << 4));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Iterations 0 .. n_items, one barrier each (both roles run the same
+  // sequence): the score waves fold item it, the gradient waves item it-1.
+  auto ring = [&](auto&& body) {
+    for (int i = 0; i <= AHEAD; ++i) issue_item(i);
+    wait_items_and_sync();   // item 0 resident
+    for (int it = 0; it <= n_items; ++it) {
+      issue_item(it + AHEAD + 1);   // buffer of item it-2, whose last reader finished before the last barrier
+      body(it);
+      wait_items_and_sync();        // items up to it+1 resident; this iteration's LDS traffic done
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // drain the clamped prefetches before the waves leave
+  };
+  typedef const __attribute__((address_space(3))) float lds_f32;
+  typedef const f32x4 __attribute__((address_space(3)))* lds_f4_ptr;
+  typedef bf16x8 __attribute__((address_space(3)))* lds_frag_wptr;
+  if (n_items == 0) return;   // dK, dV of these keys receive nothing from this visit
 
-    // S = Q K^T and dP = dO V^T of an item: lane holds key l32, register r
-    // query 8(r/4) + 4hi + r%4.
-    auto scores = [&](const lds_t* b, f32x16& s, f32x16& dp) {
+  if (scorer) {
+    // K and V fragments (B operand: key l32, d = 16ks + 8hi ..).
+    bf16x8 kf[KS], vf[KS];
+    {
+      const bool kb = key < a.b;
+      const size_t base = ((size_t)(kb ? key : 0) * a.Hkv + kvh) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 zk, zv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zk[e] = zv[e] = (__bf16)0.0f;
+        kf[ks] = kb ? *reinterpret_cast<const bf16x8*>(a.k + base + ks * 16 + hi * 8) : zk;
+        vf[ks] = kb ? *reinterpret_cast<const bf16x8*>(a.v + base + ks * 16 + hi * 8) : zv;
+      }
+    }
+    ring([&](int it) {
+      if (it >= n_items) return;
+      const lds_t* cur = buf(it);
+      // S = Q K^T and dP = dO V^T: lane holds key l32, register r query
+      // 8(r/4) + 4hi + r%4.
+      f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<lds_frag_ptr>(b + IT::QK + rowtile_off(l32, ks * 2 + hi));
-        const bf16x8 da = *reinterpret_cast<lds_frag_ptr>(b + IT::DOK + rowtile_off(l32, ks * 2 + hi));
-        s = mfma(qa, kf[ks], s);
-        dp = mfma(da, vf[ks], dp);
+        s = mfma(F::row(cur + IT::QK, ks, l32, hi), kf[ks], s);
+        dp = mfma(F::row(cur + IT::DOK, ks, l32, hi), vf[ks], dp);
       }
-    };
-
-    issue_item(0);
-    issue_item(1);
-    issue_item(2);
-    wait_items_and_sync(std::integral_constant<int, 1>{});   // items 0, 1 resident
-    f32x16 s, dp;
-    scores(buf(0), s, dp);
-
-    for (int it = 0; it < n_items; ++it) {
-      const lds_t* cur = buf(it);
-      issue_item(it + 3);   // buffer of item it-1, whose reads ended before the last barrier
-      const int q0 = (pb_lo + it / a.G) * 32;
-
-      // P = exp2(S log2e/sqrt(d) - lse2), dS = P (dP - D) of item it.
-      typedef const __attribute__((address_space(3))) float lds_f32;
-      typedef const f32x4 __attribute__((address_space(3)))* lds_f4_ptr;
       lds_f32* st = (lds_f32*)(cur + IT::STATS);
       f32x16 p, ds;
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const f32x4 l2 = *(lds_f4_ptr)(st + 8 * rg + 4 * hi);
         const f32x4 dd = *(lds_f4_ptr)(st + 32 + 8 * rg + 4 * hi);
-        const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-        const float dvv[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = rg * 4 + x;
-          p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -lv[x]));
-          ds[r] = p[r] * (dp[r] - dvv[x]);
+          p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -l2[x]));
+          ds[r] = p[r] * (dp[r] - dd[x]);
         }
       }
+      const int q0 = (pb_lo + it / a.G) * 32;
       if (q0 < full_from || q0 + 31 >= a.b) {   // wave-uniform: some pair of the item is masked
         const int lo = thr - q0, hiq = a.b - q0;
 #pragma unroll
@@ -379,36 +412,45 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
           ds[r] = ok ? ds[r] : 0.f;
         }
       }
-      const bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
-      const bf16x8 db0 = pack8(ds, 0), db1 = pack8(ds, 8);
-
-      // Scores of item it+1 (past the last item: a clamped copy, unused).
-      scores(buf(it + 1), s, dp);
-
-      // dV^T += dO^T P and dK^T += Q^T dS of item it (A: transposed tiles, row d = 32dt + l32).
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int drow = dt * 32 + l32;
-        const bf16x8 o0 = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOV + coltile_off<D>(drow, 0 + hi));
-        const bf16x8 o1 = *reinterpret_cast<lds_frag_ptr>(cur + IT::DOV + coltile_off<D>(drow, 2 + hi));
-        const bf16x8 q0f = *reinterpret_cast<lds_frag_ptr>(cur + IT::QV + coltile_off<D>(drow, 0 + hi));
-        const bf16x8 q1f = *reinterpret_cast<lds_frag_ptr>(cur + IT::QV + coltile_off<D>(drow, 2 + hi));
-        dv[dt] = mfma(o0, pb0, dv[dt]);
-        dv[dt] = mfma(o1, pb1, dv[dt]);
-        dk[dt] = mfma(q0f, db0, dk[dt]);
-        dk[dt] = mfma(q1f, db1, dk[dt]);
-      }
-      // Items it+1 and it+2 resident for the next iteration (it+3 may stay in
-      // flight); every LDS read of this iteration done before item it+4 may
-      // refill buffer it.
-      wait_items_and_sync(std::integral_constant<int, 1>{});
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // drain the clamped prefetches before the waves leave
+      // P, dS in the score register order, one 16-byte chunk per lane per
+      // group of 8 registers: chunk j of lane l at (64 j + l) * 16.
+      lds_t* xo = xch + (it & 1) * (kDkvPairs * kXchBytes) + pair * kXchBytes;
+      *reinterpret_cast<lds_frag_wptr>(xo + (0 * 64 + lane) * 16) = pack8(p, 0);
+      *reinterpret_cast<lds_frag_wptr>(xo + (1 * 64 + lane) * 16) = pack8(p, 8);
+      *reinterpret_cast<lds_frag_wptr>(xo + (2 * 64 + lane) * 16) = pack8(ds, 0);
+      *reinterpret_cast<lds_frag_wptr>(xo + (3 * 64 + lane) * 16) = pack8(ds, 8);
+    });
+    return;
   }
 
-store:
-  // Add into the caller's dK_r, dV_r: lane holds key l32, register r
-  // d = 32dt + 8(r/4) + 4hi + r%4 (4 consecutive d per group).
+  // Gradient wave: dK^T, dV^T accumulators (lane: key l32, register r:
+  // d = 32dt + 8(r/4) + 4hi + r%4).
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.f;
+  ring([&](int it) {
+    if (it < 1) return;
+    // dV^T += dO^T P and dK^T += Q^T dS of item it-1.
+    const lds_t* prev = buf(it - 1);
+    const lds_t* xi = xch + ((it - 1) & 1) * (kDkvPairs * kXchBytes) + pair * kXchBytes;
+    bf16x8 pb[2], db[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      pb[kk] = *reinterpret_cast<lds_frag_ptr>(xi + ((0 + kk) * 64 + lane) * 16);
+      db[kk] = *reinterpret_cast<lds_frag_ptr>(xi + ((2 + kk) * 64 + lane) * 16);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        dv[dt] = mfma(F::tr(prev + IT::DOK, dt, kk, lane), pb[kk], dv[dt]);
+        dk[dt] = mfma(F::tr(prev + IT::QK, dt, kk, lane), db[kk], dk[dt]);
+      }
+  });
+
+  // Add into the caller's dK_r, dV_r (4 consecutive d per register group).
   if (key >= a.b) return;
   const float sc = a.scale;
   float* dkr = a.dk + ((size_t)key * a.Hkv + kvh) * D;
@@ -582,7 +624,7 @@ hipError_t launch_bwd_pack(const __bf16* k_shard, const __bf16* v_shard, void* s
 }
 
 hipError_t launch_bwd_step(const BwdArgs& a, int D, hipStream_t st) {
-  const int nkb = (a.b + 32 * kDkvWaves - 1) / (32 * kDkvWaves);
+  const int nkb = (a.b + 32 * kDkvPairs - 1) / (32 * kDkvPairs);
   const dim3 gkv((unsigned)((nkb * a.Hkv + kXcds - 1) / kXcds * kXcds));
   const dim3 gq((unsigned)(a.dq_wgs_per_head * a.Hkv));
   if (D == 128) {
