@@ -5,8 +5,10 @@
 //   m* = max_i m_i,  w_i = exp(m_i - m*),  O = sum w_i y_i / sum w_i z_i,
 //   LSE = m* + ln sum w_i z_i.
 // A streaming, HBM-bound kernel: every y element is read once.  D/4 lanes own
-// one (head, row) pair, each a float4 slice of d; pairs are taken head-major so
-// that the m and z reads of neighbouring pairs are contiguous.
+// one (row, head) pair, each a float4 slice of d; pairs are taken row-major, so
+// the workgroups in flight read y (and write the output) as one contiguous
+// stream.  The m and z reads of neighbouring pairs are a row apart; the
+// workgroups of the next rows take the rest of each line from L2.
 #include "internal.h"
 
 namespace ringattn {
@@ -19,13 +21,13 @@ template <int D, bool F32OUT>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ m, const float* __restrict__ z,
                                                     const float* __restrict__ y, int nparts, int64_t rows,
                                                     int Hq, void* __restrict__ out, float* __restrict__ lse) {
-  constexpr int TP = D / 4;              // lanes per (head, row) pair
+  constexpr int TP = D / 4;              // lanes per (row, head) pair
   constexpr int PPB = 256 / TP;          // pairs per block
   const int64_t pair = (int64_t)blockIdx.x * PPB + threadIdx.x / TP;
   const int l4 = threadIdx.x % TP;
   if (pair >= rows * (int64_t)Hq) return;
-  const int h = (int)(pair / rows);
-  const int64_t row = pair - (int64_t)h * rows;
+  const int64_t row = pair / Hq;
+  const int h = (int)(pair - row * Hq);
 
   const size_t part_mz = (size_t)Hq * rows;               // stride between parts of m, z
   const size_t part_y = (size_t)rows * Hq * D;            // stride between parts of y
