@@ -182,13 +182,6 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t* __restric
   }
 }
 
-// Direct global -> LDS copy of `chunks` 1 KB chunks, spread over `waves` waves.
-__device__ __forceinline__ void load_chunks(const unsigned char* g, lds_t* l, int chunks, int waves, int wave,
-                                            int lane) {
-  for (int c = wave; c < chunks; c += waves)
-    __builtin_amdgcn_global_load_lds(g + c * 1024 + lane * 16, l + c * 1024, 16, 0, 0);
-}
-
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   bf16x8 r;
 #pragma unroll
@@ -481,13 +474,38 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
 
 constexpr int kDqWaves = 8;    // 8 query items (32 rows each) per workgroup, one key/value head
 
+// An empty volatile statement that takes an MFMA result: the MFMA may no
+// longer sink below the LDS reads and VALU work that follow it.
+__device__ __forceinline__ void pin(const f32x16& acc) { asm volatile("" ::"v"(acc)); }
+
+// dQ of the rank's query rows.  A wave owns one query item (its Q and dO
+// fragments in registers, dQ^T accumulators); the workgroup's 8 items share
+// one key/value head and stream the visiting block's 64-key tiles through
+// LDS: K and V row-major (the A operands of S^T = K Q^T and dP^T = V dO^T)
+// and K^T (the A operand of dQ^T += K^T dS^T), three buffers each.
+// Iteration t computes tile t in two half tiles of 32 keys while K(t+2),
+// V(t+2) and K^T(t+1) stream in.
+//
+// Tiles that every row of the workgroup sees in full run in a software
+// pipeline over half tiles h: block h issues the 8 MFMAs of dQ(h-1) with the
+// VALU work of half h in between (dS = P (dP - D), P = exp2(S log2e/sqrt(d) -
+// lse2), packed to bf16), then the 16 MFMAs of S, dP of half h+1 into the same
+// registers.  Each MFMA is followed by the LDS read of the fragment a later
+// MFMA takes.  The remaining tiles (causal diagonal, key end, shard end) are
+// folded one half at a time with the element mask.
 template <int D>
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   using KB = KBlock<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[2 * KB::BYTES];
+  constexpr int CT = KB::TILE / 1024;   // 1 KB chunks of one component tile
+  static_assert(CT % kDqWaves == 0, "component tiles split evenly over the waves");
+  constexpr int PWC = CT / kDqWaves;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[9 * KB::TILE];
   lds_t* smem = (lds_t*)smem_raw;
+  auto kbuf = [&](int t) { return smem + (t % 3) * KB::TILE; };
+  auto vbuf = [&](int t) { return smem + (3 + t % 3) * KB::TILE; };
+  auto tbuf = [&](int t) { return smem + (6 + t % 3) * KB::TILE; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -506,9 +524,12 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
   auto keys_of = [&](int i) {
     return i < a.qbeg ? 0 : (a.shift < 0 ? a.kend : max(0, min(a.kend, i + 1 - a.shift)));
   };
-  const int last_item = min(wgi * kDqWaves + kDqWaves - 1, items - 1);
+  const int first_item = wgi * kDqWaves;
+  const int last_item = min(first_item + kDqWaves - 1, items - 1);
   const int T = (keys_of(min((last_item / a.G) * 32 + 32, a.b) - 1) + kKeyTile - 1) / kKeyTile;
   const int my_tiles = active ? (keys_of(min(q0 + 32, a.b) - 1) + kKeyTile - 1) / kKeyTile : 0;
+  // Tiles every row of the workgroup sees in full (its first row has the fewest keys).
+  const int F = min(T, keys_of((first_item / a.G) * 32) / kKeyTile);
 
   // Q and dO fragments (B operand: query l32, d = 16ks + 8hi ..), row stats.
   bf16x8 qf[KS], df[KS];
@@ -534,25 +555,151 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
 
   const size_t head_tiles = (size_t)(a.bpad / kKeyTile);
   const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.kslot) + (size_t)kvh * head_tiles * KB::BYTES;
-  if (T > 0) load_chunks(kg, smem, KB::CHUNKS, kDqWaves, wave, lane);
+  // Direct loads of one component (offset KB::K, KB::V or KB::KT) of tile t,
+  // the source clamped to the last tile (a prefetch past the end reads valid
+  // memory into a buffer that is read only for discarded products).
+  auto issue = [&](int t, int comp, lds_t* dst) {
+    const unsigned char* g = kg + (size_t)min(t, T - 1) * KB::BYTES + comp;
+#pragma unroll
+    for (int i = 0; i < PWC; ++i) {
+      const int c = wave * PWC + i;
+      load_lds16(g + c * 1024 + lane * 16, dst + c * 1024);
+    }
+  };
+  auto begin_iter = [&](int t) {
+    issue(t + 2, KB::K, kbuf(t + 2));
+    issue(t + 2, KB::V, vbuf(t + 2));
+    issue(t + 1, KB::KT, tbuf(t + 1));
+  };
+
+  if (T > 0) {
+    issue(0, KB::K, kbuf(0));
+    issue(0, KB::V, vbuf(0));
+    issue(1, KB::K, kbuf(1));
+    issue(1, KB::V, vbuf(1));
+    issue(0, KB::KT, tbuf(0));
+  }
   wait_all_and_sync();
 
-  for (int t = 0; t < T; ++t) {
-    lds_t* cur = smem + (t & 1) * KB::BYTES;
-    if (t + 1 < T) load_chunks(kg + (size_t)(t + 1) * KB::BYTES, smem + ((t + 1) & 1) * KB::BYTES, KB::CHUNKS, kDqWaves, wave, lane);
+  // Fragments: key / value tile rows (row = 32 half + l32, chunk 2ks + hi) and
+  // K^T rows (d = 32dt + l32, keys of k-step kk of half `half`).
+  auto kfrag = [&](const lds_t* b, int half, int ks) {
+    return *reinterpret_cast<lds_frag_ptr>(b + key_tile_off(half * 32 + l32, ks * 2 + hi));
+  };
+  auto tfrag = [&](const lds_t* b, int half, int dt, int kk) {
+    return *reinterpret_cast<lds_frag_ptr>(b + val_tile_off<D>(dt * 32 + l32, (half * 2 + kk) * 2 + hi));
+  };
+
+  int t = 0;
+  if (F > 0) {
+    constexpr int NG = 2 * DT + 2 * KS;   // MFMAs per half-tile block
+    constexpr int kPF = 4;                // fragment prefetch distance, in groups
+    constexpr int per = 16 / (2 * DT);    // VALU units per dQ group
+    f32x16 s, dp;
+    bf16x8 dsA[2], dsB[2];
+    bf16x8 fr[kPF];
+    // S, dP of half 0 of tile 0; no pending dQ (zero dS against a resident tile).
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma(kfrag(kbuf(0), 0, ks), qf[ks], s);
+      dp = mfma(kfrag(vbuf(0), 0, ks), df[ks], dp);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsB[kk][e] = (__bf16)0.0f;
+#pragma unroll
+    for (int j = 0; j < kPF; ++j) fr[j] = tfrag(tbuf(0), 0, j / 2, j % 2);
+
+    // One half-tile block.  Block h = 2t + half: dQ of block h-1 from K^T of
+    // (tp, hp) with dsp; S, dP of block h+1 from K, V of (tn, hn); VALU of
+    // block h into dsc.  The fragments of the next block's first kPF groups
+    // are K^T of (t, half) (the next block's dQ is dQ(h)).
+    auto block = [&](int t, int half, const bf16x8 (&dsp)[2], bf16x8 (&dsc)[2]) {
+      const int tp = half ? t : t - 1, hp = half ? 0 : 1;   // block h-1
+      const int tn = half ? t + 1 : t, hn = half ? 0 : 1;   // block h+1
+      const lds_t* tb_prev = tbuf(tp < 0 ? 0 : tp);
+      const lds_t* tb_cur = tbuf(t);
+      const lds_t* kb_next = kbuf(tn);
+      const lds_t* vb_next = vbuf(tn);
+      float pv[16], dsv[16];
+      auto frag = [&](int m) -> bf16x8 {
+        if (m < 2 * DT) return tfrag(tb_prev, hp, m / 2, m % 2);
+        if (m < 2 * DT + KS) return kfrag(kb_next, hn, m - 2 * DT);
+        if (m < NG) return kfrag(vb_next, hn, m - 2 * DT - KS);
+        return tfrag(tb_cur, half, (m - NG) / 2, (m - NG) % 2);
+      };
+      auto unit = [&](int e) {
+        const float x = __builtin_amdgcn_exp2f(fmaf(s[e], a.sl2, -l2));
+        pv[e] = x;
+        dsv[e] = x * (dp[e] - drow);
+        if (e & 1) {
+          const f32x2 qq = {dsv[e - 1], dsv[e]};
+          const bf16x2 pk = __builtin_convertvector(qq, bf16x2);
+          dsc[e >> 3][(e & 7) - 1] = pk[0];
+          dsc[e >> 3][e & 7] = pk[1];
+        }
+      };
+      auto group = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        bf16x8& f = fr[m % kPF];
+        if constexpr (m < 2 * DT) {
+          o[m / 2] = mfma(f, dsp[m % 2], o[m / 2]);
+          pin(o[m / 2]);
+#pragma unroll
+          for (int u = 0; u < per; ++u) unit(m * per + u);
+        } else if constexpr (m < 2 * DT + KS) {
+          constexpr int ks = m - 2 * DT;
+          if constexpr (ks == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = 0.f;
+          }
+          s = mfma(f, qf[ks], s);
+          pin(s);
+        } else {
+          constexpr int ks = m - 2 * DT - KS;
+          if constexpr (ks == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+          }
+          dp = mfma(f, df[ks], dp);
+          pin(dp);
+        }
+        f = frag(m + kPF);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      [&]<int... ms>(std::integer_sequence<int, ms...>) { (group(std::integral_constant<int, ms>{}), ...); }
+      (std::make_integer_sequence<int, NG>{});
+    };
+
+    for (; t < F; ++t) {
+      begin_iter(t);
+      block(t, 0, dsB, dsA);
+      block(t, 1, dsA, dsB);
+      wait_all_and_sync();
+    }
+    // dQ of the last fast block (tile F-1, half 1); the S, dP it formed for
+    // tile F are discarded.
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) o[dt] = mfma(tfrag(tbuf(F - 1), 1, dt, kk), dsB[kk], o[dt]);
+  }
+
+  for (; t < T; ++t) {
+    begin_iter(t);
     if (t < my_tiles) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int row = half * 32 + l32;
         f32x16 s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<lds_frag_ptr>(cur + KB::K + key_tile_off(row, ks * 2 + hi));
-          const bf16x8 va = *reinterpret_cast<lds_frag_ptr>(cur + KB::V + key_tile_off(row, ks * 2 + hi));
-          s = mfma(ka, qf[ks], s);
-          dp = mfma(va, df[ks], dp);
+          s = mfma(kfrag(kbuf(t), half, ks), qf[ks], s);
+          dp = mfma(kfrag(vbuf(t), half, ks), df[ks], dp);
         }
         // Lane holds query qi, register r key t*64 + 32 half + 8(r/4) + 4hi + r%4.
         f32x16 ds;
@@ -566,11 +713,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
         const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 8);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int dr = dt * 32 + l32;
-          const bf16x8 k0f = *reinterpret_cast<lds_frag_ptr>(cur + KB::KT + val_tile_off<D>(dr, (half * 2 + 0) * 2 + hi));
-          const bf16x8 k1f = *reinterpret_cast<lds_frag_ptr>(cur + KB::KT + val_tile_off<D>(dr, (half * 2 + 1) * 2 + hi));
-          o[dt] = mfma(k0f, d0, o[dt]);
-          o[dt] = mfma(k1f, d1, o[dt]);
+          o[dt] = mfma(tfrag(tbuf(t), half, dt, 0), d0, o[dt]);
+          o[dt] = mfma(tfrag(tbuf(t), half, dt, 1), d1, o[dt]);
         }
       }
     }
