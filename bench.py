@@ -13,6 +13,8 @@ step.  ``roofline`` reports the step kernel against the MI355X bf16 dense MFMA
 peak, with its average launch duration measured by HIP events around every step
 kernel inside the timed region.  ``cpu_baseline`` times the fp64 oracle on the
 host cores on a bounded sample of query rows of the same workload.
+``other_workloads`` times the forward on the other named bf16 workloads (the
+striped and zigzag layouts, 32k and 128k shares).
 ``reference_gemm`` times the vendor's dense bf16 GEMM on the same GPU (the
 practical dense-MFMA rate under sustained load, for context).
 ``merge_kernel`` and ``decode_kernel`` report the two HBM-bound kernels (the
@@ -24,7 +26,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--cpu-seconds S] [--no-cpu-baseline] [--no-merge]
                        [--no-decode] [--decode-workload NAME] [--decode-only]
                        [--no-backward] [--backward-workload NAME] [--backward-only]
-                       [--no-gemm-ref]
+                       [--no-gemm-ref] [--no-workloads]
 """
 
 from __future__ import annotations
@@ -226,6 +228,47 @@ def measure_merge(reps: int = 10) -> dict:
             "frac": gbs / PEAK_HBM_GBS, "launches": t["merge_launches"]}
 
 
+OTHER_WORKLOADS = ("32k-contiguous-causal", "32k-striped-causal", "32k-zigzag-causal", "128k-contiguous-causal",
+                   "1m-zigzag-causal")
+
+
+def measure_workloads(names=OTHER_WORKLOADS, reps: int = 3) -> list:
+    """The forward call on the other named bf16 workloads (the other shard
+    layouts and sizes), timed like the main line: useful TFLOP/s per call."""
+    import torch
+
+    import ring_attention_block_step_amd as ra
+    import workloads as wl
+
+    res = []
+    for name in names:
+        w = wl.WORKLOADS[name]
+        rank = w.ranks[-1]
+        k_glob, v_glob = wl.global_kv(w)
+        idx = ra.shard_index(w.N, w.P, w.layout, rank)
+        q = wl.query_rows(w, idx.numpy()).cuda()
+        k = ra.pack_shards(k_glob, w.P, w.layout).cuda()
+        v = ra.pack_shards(v_glob, w.P, w.layout).cuda()
+        del k_glob, v_glob
+        out = torch.empty_like(q)
+        lse = torch.empty((w.Hq, w.b), dtype=torch.float32, device="cuda")
+        ra.forward(q, k, v, P=w.P, rank=rank, causal=w.causal, layout=w.layout, out=out, lse=lse)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            ra.forward(q, k, v, P=w.P, rank=rank, causal=w.causal, layout=w.layout, out=out, lse=lse)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = useful_flops(useful_pairs(w.layout, rank, w.P, w.b, w.causal), w.d, w.Hq)
+        res.append({"workload": name, "layout": w.layout, "rank": rank, "ms_per_call": ms,
+                    "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s"})
+        del q, k, v, out, lse
+    return res
+
+
 def measure_reference_gemm(n: int = 16384, reps: int = 10) -> dict:
     """Context for the MFMA roofline, not a step of the path: the vendor
     library's dense bf16 GEMM (torch.matmul, which dispatches to hipBLASLt) on
@@ -370,6 +413,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true", help="skip the merge-kernel measurement")
     ap.add_argument("--no-gemm-ref", action="store_true", help="skip the vendor bf16 GEMM reference measurement")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the forward on the other named workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-kernel measurement")
     ap.add_argument("--decode-workload", default="decode-31k-gqa64",
                     help="decode workload of the decode-kernel measurement")
@@ -471,6 +515,7 @@ def main(argv=None) -> int:
 
     merge = None if args.no_merge else measure_merge()
     gemm = None if args.no_gemm_ref else measure_reference_gemm()
+    others = None if args.no_workloads else measure_workloads()
     decode = None if args.no_decode else measure_decode(args.decode_workload)
     backward = None if args.no_backward else measure_backward(args.backward_workload)
 
@@ -498,6 +543,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity_sample": parity,
+        "other_workloads": others,
         "reference_gemm": gemm,
         "step_kernel_vs_reference_gemm": (achieved / gemm["value"]) if (gemm and achieved) else None,
         "merge_kernel": merge,
