@@ -182,6 +182,10 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t* __restric
   }
 }
 
+// An empty volatile statement that takes an MFMA result: the MFMA may no
+// longer sink below the LDS reads and VALU work that follow it.
+__device__ __forceinline__ void pin(const f32x16& acc) { asm volatile("" ::"v"(acc)); }
+
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
   bf16x8 r;
 #pragma unroll
@@ -258,10 +262,12 @@ struct ItemFrag {
 //   the gradient wave (dK^T, dV^T accumulators) takes them one item later and
 //                    folds dV^T += dO^T P and dK^T += Q^T dS, with the
 //                    transposed operands read from the same item tiles.
-// Two waves per SIMD, each within 256 registers, so the matrix cores of one
-// overlap the vector work of the other.  Items rotate through a ring of
-// kDkvBufs LDS buffers: in iteration it the score waves read item it, the
-// gradient waves item it-1, and items it+1 .. it+4 are resident or in flight.
+// Two waves per SIMD, each within 256 registers.  The score wave runs a
+// pipeline over items: in iteration it the MFMAs of item it+1 alternate with
+// the VALU work of item it, so its matrix work also overlaps its own vector
+// work.  Items rotate through a ring of kDkvBufs LDS buffers: in iteration it
+// the score waves read items it and it+1, the gradient waves item it-1, and
+// items it+2 .. it+4 are resident or in flight.
 template <int D>
 __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
@@ -303,17 +309,22 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   const int full_from =
       (plast < a.b && plast < a.kend) ? (a.shift >= 0 ? max(a.qbeg, plast + a.shift) : a.qbeg) : INT_MAX;
 
-  // Item it lands in buffer it % kDkvBufs.  The source index is clamped to
-  // the last item, so a prefetch past the end reads a valid block into a
-  // buffer no later iteration reads.  Chunk c of a block goes to wave
-  // c % kDkvWaves, so the first CHUNKS % kDkvWaves waves copy one more.
-  constexpr int PWX = (IT::CHUNKS + kDkvWaves - 1) / kDkvWaves;
-  constexpr int PW = IT::CHUNKS / kDkvWaves;
-  constexpr int NX = IT::CHUNKS - PW * kDkvWaves;   // waves that copy PWX chunks
-  constexpr int AHEAD = 3;                          // items left in flight at each barrier
+  // Item it lands in buffer it % kDkvBufs.  Only the score waves copy (a
+  // wave with direct-to-LDS loads in flight would have to wait for them before
+  // its own LDS reads).  The source index is clamped to the last item, so a
+  // prefetch past the end reads a valid block into a buffer that is read only
+  // for discarded products.  Chunk c of a block goes to score wave
+  // c % kDkvPairs, so the first CHUNKS % kDkvPairs waves copy one more.
+  constexpr int PWX = (IT::CHUNKS + kDkvPairs - 1) / kDkvPairs;
+  constexpr int PW = IT::CHUNKS / kDkvPairs;
+  constexpr int NX = IT::CHUNKS - PW * kDkvPairs;   // score waves that copy PWX chunks
+  constexpr int AHEAD = 2;                          // items left in flight at each barrier
+  constexpr int DIST = AHEAD + 2;                   // iteration it issues item it + DIST
   static_assert(AHEAD * PWX < 16, "vmcnt immediate");
+  static_assert(kDkvBufs >= DIST + 2, "items it-1 .. it+DIST live in iteration it");
   auto buf = [&](int it) { return smem + (it % kDkvBufs) * IT::BYTES; };
   auto issue_item = [&](int it) {
+    if (!scorer) return;
     const int src = min(it, n_items - 1);
     const int pb = pb_lo + src / a.G;
     const int hq = kvh * a.G + src % a.G;
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
     lds_t* l = buf(it);
 #pragma unroll
     for (int i = 0; i < PWX; ++i) {
-      const int c = wave + kDkvWaves * i;
+      const int c = wave + kDkvPairs * i;
       if (i < PW || c < IT::CHUNKS) load_lds16(g + c * 1024 + lane * 16, l + c * 1024);
     }
   };
@@ -330,23 +341,26 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   auto wait_items_and_sync = [&]() {
     if (wave < NX)
       __builtin_amdgcn_s_waitcnt((AHEAD * PWX) | (7 << 4));
-    else
+    else if (scorer)
       __builtin_amdgcn_s_waitcnt((AHEAD * PW) | (7 << 4));
+    else
+      __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // Iterations 0 .. n_items, one barrier each (both roles run the same
-  // sequence): the score waves fold item it, the gradient waves item it-1.
-  auto ring = [&](auto&& body) {
-    for (int i = 0; i <= AHEAD; ++i) issue_item(i);
-    wait_items_and_sync();   // item 0 resident
-    for (int it = 0; it <= n_items; ++it) {
-      issue_item(it + AHEAD + 1);   // buffer of item it-2, whose last reader finished before the last barrier
-      body(it);
-      wait_items_and_sync();        // items up to it+1 resident; this iteration's LDS traffic done
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // drain the clamped prefetches before the waves leave
+  // Both roles run the same sequence of barriers: a prologue that leaves
+  // items 0 and 1 resident, then iterations 0 .. n_items, each issuing item
+  // it + DIST (into the buffer of item it-2, whose last reader finished
+  // before the previous barrier) and ending with items up to it+2 resident.
+  auto prologue = [&]() {
+    for (int i = 0; i < DIST; ++i) issue_item(i);
+    wait_items_and_sync();
+  };
+  auto iteration = [&](int it, auto&& body) {
+    issue_item(it + DIST);
+    body(it);
+    wait_items_and_sync();
   };
   typedef const __attribute__((address_space(3))) float lds_f32;
   typedef const f32x4 __attribute__((address_space(3)))* lds_f4_ptr;
@@ -368,51 +382,108 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
         vf[ks] = kb ? *reinterpret_cast<const bf16x8*>(a.v + base + ks * 16 + hi * 8) : zv;
       }
     }
-    ring([&](int it) {
-      if (it >= n_items) return;
+    // S = Q K^T and dP = dO V^T of an item: lane holds key l32, register r
+    // query 8(r/4) + 4hi + r%4.  Two register sets: iteration it turns the
+    // set of item it into P and dS while the MFMAs of item it+1 fill the
+    // other.  The 2KS MFMAs alternate S and dP; each is followed by one
+    // register's VALU work and the LDS read of the fragment kPF MFMAs later.
+    constexpr int NM = 2 * KS;
+    constexpr int kPF = 4;
+    constexpr int UPG = NM >= 16 ? 1 : 16 / NM;   // registers of P, dS per MFMA
+    static_assert(UPG * NM >= 16, "every register of P, dS is formed");
+    auto frag = [&](const lds_t* b, int m) { return F::row(b + (m & 1 ? IT::DOK : IT::QK), m >> 1, l32, hi); };
+    f32x16 sA, dA, sB, dB;
+
+    auto step = [&](int it, f32x16& cs, f32x16& cd, f32x16& ns, f32x16& nd, auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
       const lds_t* cur = buf(it);
-      // S = Q K^T and dP = dO V^T: lane holds key l32, register r query
-      // 8(r/4) + 4hi + r%4.
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma(F::row(cur + IT::QK, ks, l32, hi), kf[ks], s);
-        dp = mfma(F::row(cur + IT::DOK, ks, l32, hi), vf[ks], dp);
-      }
+      const lds_t* nxt = buf(it + 1);
       lds_f32* st = (lds_f32*)(cur + IT::STATS);
-      f32x16 p, ds;
+      f32x4 l2v[4], ddv[4];
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 l2 = *(lds_f4_ptr)(st + 8 * rg + 4 * hi);
-        const f32x4 dd = *(lds_f4_ptr)(st + 32 + 8 * rg + 4 * hi);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r = rg * 4 + x;
-          p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.sl2, -l2[x]));
-          ds[r] = p[r] * (dp[r] - dd[x]);
-        }
+        l2v[rg] = *(lds_f4_ptr)(st + 8 * rg + 4 * hi);
+        ddv[rg] = *(lds_f4_ptr)(st + 32 + 8 * rg + 4 * hi);
       }
-      const int q0 = (pb_lo + it / a.G) * 32;
-      if (q0 < full_from || q0 + 31 >= a.b) {   // wave-uniform: some pair of the item is masked
-        const int lo = thr - q0, hiq = a.b - q0;
+      bf16x8 fr[kPF];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+      for (int j = 0; j < kPF; ++j) fr[j] = frag(nxt, j);
+      const int q0 = (pb_lo + it / a.G) * 32;
+      const int lo = thr - q0, hiq = a.b - q0;
+      bf16x8 pk[2], dk8[2];
+      auto unit = [&](int r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(cs[r], a.sl2, -l2v[r >> 2][r & 3]));
+        float g = p * (cd[r] - ddv[r >> 2][r & 3]);
+        if constexpr (MASKED) {
           const int c = 8 * (r >> 2) + 4 * hi + (r & 3);
           const bool ok = c >= lo && c < hiq;
-          p[r] = ok ? p[r] : 0.f;
-          ds[r] = ok ? ds[r] : 0.f;
+          p = ok ? p : 0.f;
+          g = ok ? g : 0.f;
         }
-      }
+        cs[r] = p;
+        cd[r] = g;
+        if (r & 1) {
+          const f32x2 pp = {cs[r - 1], p}, gg = {cd[r - 1], g};
+          const bf16x2 a2 = __builtin_convertvector(pp, bf16x2), b2 = __builtin_convertvector(gg, bf16x2);
+          pk[r >> 3][(r & 7) - 1] = a2[0];
+          pk[r >> 3][r & 7] = a2[1];
+          dk8[r >> 3][(r & 7) - 1] = b2[0];
+          dk8[r >> 3][r & 7] = b2[1];
+        }
+      };
+      auto group = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int ks = m >> 1;
+        bf16x8& f = fr[m % kPF];
+        if constexpr (m & 1) {
+          if constexpr (ks == 0) nd = mfma(f, vf[0], f32x16{});
+          else nd = mfma(f, vf[ks], nd);
+          pin(nd);
+        } else {
+          if constexpr (ks == 0) ns = mfma(f, kf[0], f32x16{});
+          else ns = mfma(f, kf[ks], ns);
+          pin(ns);
+        }
+#pragma unroll
+        for (int u = 0; u < UPG; ++u)
+          if (m * UPG + u < 16) unit(m * UPG + u);
+        if constexpr (m + kPF < NM) f = frag(nxt, m + kPF);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      [&]<int... ms>(std::integer_sequence<int, ms...>) { (group(std::integral_constant<int, ms>{}), ...); }
+      (std::make_integer_sequence<int, NM>{});
       // P, dS in the score register order, one 16-byte chunk per lane per
       // group of 8 registers: chunk j of lane l at (64 j + l) * 16.
       lds_t* xo = xch + (it & 1) * (kDkvPairs * kXchBytes) + pair * kXchBytes;
-      *reinterpret_cast<lds_frag_wptr>(xo + (0 * 64 + lane) * 16) = pack8(p, 0);
-      *reinterpret_cast<lds_frag_wptr>(xo + (1 * 64 + lane) * 16) = pack8(p, 8);
-      *reinterpret_cast<lds_frag_wptr>(xo + (2 * 64 + lane) * 16) = pack8(ds, 0);
-      *reinterpret_cast<lds_frag_wptr>(xo + (3 * 64 + lane) * 16) = pack8(ds, 8);
-    });
+      *reinterpret_cast<lds_frag_wptr>(xo + (0 * 64 + lane) * 16) = pk[0];
+      *reinterpret_cast<lds_frag_wptr>(xo + (1 * 64 + lane) * 16) = pk[1];
+      *reinterpret_cast<lds_frag_wptr>(xo + (2 * 64 + lane) * 16) = dk8[0];
+      *reinterpret_cast<lds_frag_wptr>(xo + (3 * 64 + lane) * 16) = dk8[1];
+    };
+    auto score = [&](int it, f32x16& cs, f32x16& cd, f32x16& ns, f32x16& nd) {
+      iteration(it, [&](int it) {
+        if (it >= n_items) return;
+        const int q0 = (pb_lo + it / a.G) * 32;
+        if (q0 < full_from || q0 + 31 >= a.b)   // wave-uniform: some pair of the item is masked
+          step(it, cs, cd, ns, nd, std::true_type{});
+        else
+          step(it, cs, cd, ns, nd, std::false_type{});
+      });
+    };
+    prologue();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sA[r] = dA[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      sA = mfma(frag(buf(0), 2 * ks), kf[ks], sA);
+      dA = mfma(frag(buf(0), 2 * ks + 1), vf[ks], dA);
+    }
+    for (int it = 0; it <= n_items; it += 2) {
+      score(it, sA, dA, sB, dB);
+      if (it + 1 > n_items) break;
+      score(it + 1, sB, dB, sA, dA);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // drain the clamped prefetches before the waves leave
     return;
   }
 
@@ -423,7 +494,8 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.f;
-  ring([&](int it) {
+  prologue();
+  for (int it = 0; it <= n_items; ++it) iteration(it, [&](int it) {
     if (it < 1) return;
     // dV^T += dO^T P and dK^T += Q^T dS of item it-1.
     const lds_t* prev = buf(it - 1);
@@ -473,10 +545,6 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int kDqWaves = 8;    // 8 query items (32 rows each) per workgroup, one key/value head
-
-// An empty volatile statement that takes an MFMA result: the MFMA may no
-// longer sink below the LDS reads and VALU work that follow it.
-__device__ __forceinline__ void pin(const f32x16& acc) { asm volatile("" ::"v"(acc)); }
 
 // dQ of the rank's query rows.  A wave owns one query item (its Q and dO
 // fragments in registers, dQ^T accumulators); the workgroup's 8 items share
