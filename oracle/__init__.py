@@ -34,6 +34,7 @@ from .ring_oracle import (  # noqa: F401
     allowed_mask,
     allowed_pair_count,
     backward_dense,
+    backward_sampled,
     decode_partial,
     dense_attention,
     empty_state,

@@ -318,6 +318,62 @@ def ring_backward(q_local, u: int, k, v, out, lse, dout, P: int, layout: str, ca
     return dq, dk, dv
 
 
+def backward_sampled(q_local, u: int, k, v, out, lse, dout, P: int, layout: str, causal: bool, rows, keys):
+    """Selected entries of rank u's backward share (ring_backward), each summed
+    over the whole sequence at once instead of visit by visit.
+
+    The formulas of "The backward pass costs a second ring" (transformer-math
+    page) for one query row i at global token t_i, head h (key/value head
+    g = h // G), with D_i = dO_i . O_i and, for each key token t that row i
+    may see, S = q_i . k_t / sqrt(d), p = e^{S - LSE_i}, dP = dO_i . v_t,
+    dS = p (dP - D_i):
+      dQ_i  = sum_t dS k_t / sqrt(d)
+    and for one key token t (shard r, local row j), over the rank's rows i
+    that may see it, summed over the query heads of its group:
+      dV_r[j] = sum_i p dO_i,    dK_r[j] = sum_i dS q_i / sqrt(d).
+    rows: local query rows of rank u; keys: (r, j) pairs.  Returns dq
+    [len(rows), Hq, d], dk and dv [len(keys), Hkv, d].  A row with
+    LSE = -inf saw no key and contributes nothing.
+    """
+    q_local = np.asarray(q_local, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    b, Hq, d = q_local.shape
+    N, Hkv, _ = k.shape
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    rows = np.asarray(rows, dtype=np.int64)
+    tq = shard_positions(layout, u, P, b)
+    tk = np.array([shard_positions(layout, r, P, b)[j] for r, j in keys], dtype=np.int64)
+    live = np.isfinite(lse)
+    lse_safe = np.where(live, lse, 0.0)
+    D = (dout * out).sum(axis=2).T                            # [Hq, b]
+    dq = np.zeros((rows.size, Hq, d))
+    dk = np.zeros((tk.size, Hkv, d))
+    dv = np.zeros((tk.size, Hkv, d))
+    allow_rows = allowed_mask(tq[rows], np.arange(N), causal)  # [R, N]
+    allow_keys = allowed_mask(tq, tk, causal)                  # [b, K]
+    for h in range(Hq):
+        g = h // G
+        # dQ of the selected rows against every key of the sequence.
+        s = (q_local[rows, h, :] @ k[:, g, :].T) * scale
+        p = np.where(allow_rows & live[h, rows][:, None], np.exp(s - lse_safe[h, rows][:, None]), 0.0)
+        dp = dout[rows, h, :] @ v[:, g, :].T
+        ds = p * (dp - D[h, rows][:, None])
+        dq[:, h, :] = ds @ k[:, g, :] * scale
+        # dK, dV of the selected keys from every row of the rank.
+        s = (q_local[:, h, :] @ k[tk, g, :].T) * scale
+        p = np.where(allow_keys & live[h][:, None], np.exp(s - lse_safe[h][:, None]), 0.0)
+        dv[:, g, :] += p.T @ dout[:, h, :]
+        dp = dout[:, h, :] @ v[tk, g, :].T
+        ds = p * (dp - D[h][:, None])
+        dk[:, g, :] += ds.T @ q_local[:, h, :] * scale
+    return dq, dk, dv
+
+
 # ---------------------------------------------------------------------------
 # Decode: the query passes, the key/value shard stays.
 # ---------------------------------------------------------------------------

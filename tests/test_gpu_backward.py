@@ -141,3 +141,53 @@ def test_backward_serial_and_overlapped_hops_are_bit_identical():
         res.append((gq.cpu(), gk.cpu(), gv.cpu()))
     for a, b_ in zip(*res):
         assert torch.equal(a, b_)
+
+
+@pytest.mark.parametrize("name", ["32k-contiguous-causal", "128k-contiguous-causal"])
+def test_backward_full_size_sampled(name):
+    """The workload's full share in the launch configuration the bench times
+    (rank 7 of 8 contiguous shards, 32/8 GQA, d 128), checked on sampled
+    entries: dQ of 64 local rows (0, 1, b-1 among them) and the rank's dK, dV
+    contributions to 48 keys of the diagonal shard 7 and of shards 0 and 3.
+
+    O and LSE are synthetic inputs rather than a forward's: LSE of a row at
+    global token t is ln(t + 1) + 1/2, the log-partition of unit-variance
+    scores over its t + 1 keys, and O is seeded N(0, 0.05^2).  The backward's
+    formulas hold for any such inputs, and both sides read the same values;
+    an exact forward of every row on the CPU would take minutes at 128k.
+    """
+    w = wl.WORKLOADS[name]
+    rank = w.ranks[-1]
+    b = w.b
+    tq = oracle.shard_positions(w.layout, rank, w.P, b)
+    k_glob, v_glob = wl.global_kv(w)
+    q = wl.query_rows(w, tq)
+    do = wl.token_rows(w.seed, "do", tq, w.Hq, w.d, "normal", 1.0, torch.bfloat16)
+    out = wl.token_rows(w.seed, "o", tq, w.Hq, w.d, "normal", 0.05, torch.bfloat16)
+    lse_row = np.log(tq.astype(np.float64) + 1.0) + 0.5
+    lse = torch.tensor(np.broadcast_to(lse_row, (w.Hq, b)).copy(), dtype=torch.float32)
+    print(f"[gpu] backward full size {name}: inputs ready", flush=True)
+
+    kp = ra.pack_shards(k_glob, w.P, w.layout).cuda()
+    vp = ra.pack_shards(v_glob, w.P, w.layout).cuda()
+    dk = torch.zeros(kp.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(kp.shape, dtype=torch.float32, device="cuda")
+    gq, gk, gv = ra.backward(q.cuda(), kp, vp, out.cuda(), lse.cuda(), do.cuda(), P=w.P, rank=rank,
+                             causal=w.causal, layout=w.layout, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    del kp, vp
+
+    rows = wl.sample_local_rows(b, 64, w.seed, 0)
+    keys = [(r, int(j)) for r in (7, 0, 3) for j in wl.sample_local_rows(b, 16, w.seed + r, 1)]
+    wq, wk, wv = oracle.backward_sampled(q.double().numpy(), rank, k_glob.double().numpy(),
+                                         v_glob.double().numpy(), out.double().numpy(),
+                                         lse.double().numpy(), do.double().numpy(), w.P, w.layout,
+                                         w.causal, rows, keys)
+    ridx = torch.as_tensor(rows)
+    got_q = gq[ridx].cpu().double().numpy()
+    got_k = np.stack([gk[r, j].cpu().double().numpy() for r, j in keys])
+    got_v = np.stack([gv[r, j].cpu().double().numpy() for r, j in keys])
+    _check("dq", got_q, wq, name)
+    _check("dk", got_k, wk, name)
+    _check("dv", got_v, wv, name)
+

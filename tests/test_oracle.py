@@ -579,6 +579,33 @@ def test_ring_backward_order_invariance():
             np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("layout,causal,P,b,Hq,Hkv,d", BWD_CASES)
+def test_backward_sampled_equals_ring_backward_entries(layout, causal, P, b, Hq, Hkv, d):
+    """The sampled backward (whole-sequence sums per row and per key) gives the
+    same entries as the visit-by-visit ring backward, also for O and LSE that
+    are not the forward's (any finite LSE; one row with LSE = -inf)."""
+    rng = np.random.default_rng(P * 100 + b)
+    N = P * b
+    q, k, v = _rand_qkv(rng, N, Hq, Hkv, d, scale=2.0)
+    dout = rng.standard_normal((N, Hq, d))
+    for u in range(P):
+        tq = ro.shard_positions(layout, u, P, b)
+        out = 0.3 * rng.standard_normal((b, Hq, d))
+        lse = rng.uniform(1.0, 4.0, (Hq, b))
+        lse[0, -1] = -math.inf
+        gq, gk, gv = ro.ring_backward(q[tq], u, k, v, out, lse, dout[tq], P, layout, causal)
+        rows = np.arange(b)
+        keys = [(r, j) for r in range(P) for j in range(b)]
+        sq, sk, sv = ro.backward_sampled(q[tq], u, k, v, out, lse, dout[tq], P, layout, causal, rows, keys)
+        np.testing.assert_allclose(sq, gq, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sk, gk.reshape(P * b, Hkv, d), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sv, gv.reshape(P * b, Hkv, d), rtol=0, atol=1e-12)
+        part = ro.backward_sampled(q[tq], u, k, v, out, lse, dout[tq], P, layout, causal, rows[::2], keys[1::3])
+        np.testing.assert_allclose(part[0], sq[::2], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(part[1], sk[1::3], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(part[2], sv[1::3], rtol=0, atol=1e-12)
+
+
 def _bwd_without_d_term(q_local, u, k, v, out, lse, dout, P, layout, causal, order=None):
     return _REAL_BWD(q_local, u, k, v, out * 0.0, lse, dout, P, layout, causal, order)
 

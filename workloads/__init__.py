@@ -22,7 +22,7 @@ import torch
 
 CHUNK = 256
 _MASK64 = (1 << 64) - 1
-_NAME_IDS = {"q": 1, "k": 2, "v": 3, "do": 4}   # "do": the upstream gradient dL/dO
+_NAME_IDS = {"q": 1, "k": 2, "v": 3, "do": 4, "o": 5}   # "do": the upstream gradient dL/dO; "o": a stand-in output
 
 
 def _splitmix64(x: int) -> int:
