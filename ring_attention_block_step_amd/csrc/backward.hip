@@ -12,14 +12,18 @@
 // Kernels (v_mfma_f32_32x32x16_bf16, fp32 accumulation, P and dS rounded to
 // bf16 only as MFMA operands):
 //   bwd_prep_kernel   once per call: D and LSE (log2 units) per query row,
-//                     and the query items' tiles (32 rows of one head):
-//                     Q and dO row-major (MFMA A operand of S and dP) and
-//                     Q^T, dO^T transposed with the in-group query order of
-//                     the score accumulator (A operand of dK^T and dV^T);
-//   bwd_dkdv_kernel   per visit: a wave owns 32 keys of the block (K and V
-//                     fragments in registers) and runs over every query item
-//                     that sees them: S = Q K^T, dP = dO V^T, then
-//                     dV^T += dO^T P and dK^T += Q^T dS; at the end it adds
+//                     and the query items' tiles (32 rows of one head): Q
+//                     and dO row-major with XOR-swizzled 16-byte chunks, read
+//                     both as row fragments (the A operand of S and dP) and,
+//                     with ds_read_b64_tr_b16, transposed (the A operand of
+//                     dK^T and dV^T);
+//   bwd_pack_kernel   per visit: the dQ kernel's key tiles of the visiting
+//                     block (K and V row-major, K^T);
+//   bwd_dkdv_kernel   per visit: pairs of waves own 32 keys of the block and
+//                     run over every query item that sees them: the score
+//                     wave (K and V fragments in registers) forms S = Q K^T,
+//                     dP = dO V^T, P and dS; the gradient wave folds
+//                     dV^T += dO^T P and dK^T += Q^T dS and at the end adds
 //                     into the caller's dK_r, dV_r;
 //   bwd_dq_kernel     per visit: a wave owns one query item (Q and dO
 //                     fragments in registers) and runs over the block's key
