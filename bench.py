@@ -14,7 +14,8 @@ peak, with its average launch duration measured by HIP events around every step
 kernel inside the timed region.  ``cpu_baseline`` times the fp64 oracle on the
 host cores on a bounded sample of query rows of the same workload.
 ``other_workloads`` times the forward on the other named bf16 workloads (the
-striped and zigzag layouts, 32k and 128k shares).
+striped and zigzag layouts, 32k and 128k shares), and
+``backward_other_workloads`` the backward on the 128k share.
 ``reference_gemm`` times the vendor's dense bf16 GEMM on the same GPU (the
 practical dense-MFMA rate under sustained load, for context).
 ``merge_kernel`` and ``decode_kernel`` report the two HBM-bound kernels (the
@@ -228,6 +229,7 @@ def measure_merge(reps: int = 10) -> dict:
             "frac": gbs / PEAK_HBM_GBS, "launches": t["merge_launches"]}
 
 
+BACKWARD_OTHER_WORKLOADS = ("128k-contiguous-causal",)
 OTHER_WORKLOADS = ("32k-contiguous-causal", "32k-striped-causal", "32k-zigzag-causal", "128k-contiguous-causal",
                    "1m-zigzag-causal")
 
@@ -518,6 +520,9 @@ def main(argv=None) -> int:
     others = None if args.no_workloads else measure_workloads()
     decode = None if args.no_decode else measure_decode(args.decode_workload)
     backward = None if args.no_backward else measure_backward(args.backward_workload)
+    backward_other = None
+    if not args.no_backward and not args.no_workloads:
+        backward_other = [measure_backward(n, reps=2) for n in BACKWARD_OTHER_WORKLOADS if n != args.backward_workload]
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
@@ -549,6 +554,7 @@ def main(argv=None) -> int:
         "merge_kernel": merge,
         "decode_kernel": decode,
         "backward": backward,
+        "backward_other_workloads": backward_other,
     }
     print(json.dumps(line), flush=True)
     return 0

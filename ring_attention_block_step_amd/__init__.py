@@ -1,4 +1,5 @@
-"""One device's share of a Ring Attention forward pass on MI355X (gfx950).
+"""One device's share of Ring Attention on MI355X (gfx950): the forward ring
+step, the merge of partial triples, pass-Q decode and the backward ring.
 
 Python binding of ``libringattn.so`` (C ABI: ``include/ringattn.h``).  It only
 marshals arguments: it checks torch tensors, passes their device pointers and
