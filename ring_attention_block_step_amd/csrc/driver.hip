@@ -81,10 +81,14 @@ int device_ctx(DeviceCtx** out) {
   std::lock_guard<std::mutex> lk(c.mu);
   if (!c.ready) {
     HIP_TRY(hipStreamCreateWithFlags(&c.hop, hipStreamNonBlocking));
-    HIP_TRY(hipEventCreateWithFlags(&c.ev_start, hipEventDisableTiming));
+    // The events order the two streams of one device: a device-scope release
+    // and acquire are enough, and a system-scope fence would write back and
+    // invalidate the caches at every hop.
+    const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
+    HIP_TRY(hipEventCreateWithFlags(&c.ev_start, ev_flags));
     for (int i = 0; i < 2; ++i) {
-      HIP_TRY(hipEventCreateWithFlags(&c.ev_ready[i], hipEventDisableTiming));
-      HIP_TRY(hipEventCreateWithFlags(&c.ev_done[i], hipEventDisableTiming));
+      HIP_TRY(hipEventCreateWithFlags(&c.ev_ready[i], ev_flags));
+      HIP_TRY(hipEventCreateWithFlags(&c.ev_done[i], ev_flags));
     }
     // Keep freed stream-ordered workspace in the pool between calls.
     hipMemPool_t pool;
@@ -104,7 +108,11 @@ int timing_begin(hipStream_t st, int kind) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   if (!g_timing) return -1;
   TimedLaunch t{nullptr, nullptr, kind};
-  if (hipEventCreate(&t.begin) != hipSuccess || hipEventCreate(&t.end) != hipSuccess) return -1;
+  // Timing only: no system-scope fence, which would write back and invalidate
+  // the caches around every timed kernel.
+  const unsigned flags = hipEventDisableSystemFence;
+  if (hipEventCreateWithFlags(&t.begin, flags) != hipSuccess || hipEventCreateWithFlags(&t.end, flags) != hipSuccess)
+    return -1;
   if (hipEventRecord(t.begin, st) != hipSuccess) return -1;
   g_timed.push_back(t);
   return (int)g_timed.size() - 1;
