@@ -27,7 +27,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--cpu-seconds S] [--no-cpu-baseline] [--no-merge]
                        [--no-decode] [--decode-workload NAME] [--decode-only]
                        [--no-backward] [--backward-workload NAME] [--backward-only]
-                       [--no-gemm-ref] [--no-workloads]
+                       [--no-gemm-ref] [--no-workloads] [--merge-only]
 """
 
 from __future__ import annotations
@@ -426,14 +426,15 @@ def main(argv=None) -> int:
                     help="workload of the backward measurement")
     ap.add_argument("--backward-only", action="store_true",
                     help="only run the backward measurement and print its JSON object")
+    ap.add_argument("--merge-only", action="store_true",
+                    help="only run the merge-kernel measurement and print its JSON object")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the path is one device's share of the ring; see DESIGN.md for how it would shard)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the path is one "
+              "device's share of the ring, and every GPU of a ring runs the same share", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -450,6 +451,9 @@ def main(argv=None) -> int:
         return 0
     if args.backward_only:
         print(json.dumps(measure_backward(args.backward_workload, reps=max(1, args.steps))), flush=True)
+        return 0
+    if args.merge_only:
+        print(json.dumps(measure_merge()), flush=True)
         return 0
     if args.copy_bytes:
         copy_calibration(args.copy_bytes)
