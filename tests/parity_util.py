@@ -8,6 +8,8 @@ positions it computes itself and reads key/value in global order.
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -50,6 +52,32 @@ def oracle_rows(w: wl.Workload, rank: int, local_rows: np.ndarray, k_glob, v_glo
     return oracle.dense_attention(q, tq, k, v, w.causal)
 
 
+def oracle_rows_threaded(w: wl.Workload, rank: int, local_rows: np.ndarray, k_glob, v_glob,
+                         threads: int | None = None):
+    """oracle_rows over row chunks in a thread pool (NumPy's kernels release the
+    GIL), with single-threaded BLAS inside each chunk and larger score chunks
+    than the default, so that the whole key range is streamed once per chunk
+    of rows rather than once per few rows.  Same values as oracle_rows."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    if threads is None:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    tq = oracle.shard_positions(w.layout, rank, w.P, w.b)[local_rows]
+    q = wl.query_rows(w, tq).double().numpy()
+    k = k_glob.double().numpy()
+    v = v_glob.double().numpy()
+    parts = np.array_split(np.arange(len(local_rows)), max(threads, len(local_rows) // 128))
+
+    def job(ix):
+        return oracle.dense_attention(q[ix], tq[ix], k, v, w.causal, max_chunk_elems=1 << 25)
+
+    with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(job, parts))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res], axis=1)
+
+
 def compare(w: wl.Workload, out_rows: np.ndarray, lse_rows: np.ndarray, want_o: np.ndarray,
             want_lse: np.ndarray) -> dict:
     err = np.abs(out_rows.astype(np.float64) - want_o)
@@ -76,9 +104,10 @@ def check(w: wl.Workload, stats: dict) -> None:
 
 
 def run_and_compare(w: wl.Workload, rank: int, rows_per_head: int | None = None, seed_rows: int = 0,
-                    k_glob=None, v_glob=None) -> dict:
+                    k_glob=None, v_glob=None, threaded: bool = False) -> dict:
     """Run rank's share on the GPU; compare all rows (rows_per_head None) or a
-    seeded sample of rows (the same sample for every head)."""
+    seeded sample of rows (the same sample for every head).  threaded: the
+    oracle side runs in a thread pool (large samples)."""
     if k_glob is None:
         k_glob, v_glob = wl.global_kv(w)
     q, k, v = gpu_inputs(w, rank, k_glob, v_glob)
@@ -92,7 +121,11 @@ def run_and_compare(w: wl.Workload, rank: int, rows_per_head: int | None = None,
         rows = wl.sample_local_rows(w.b, rows_per_head, w.seed + seed_rows, 0)
     out_rows = out.float().cpu().numpy()[rows]
     lse_rows = lse.cpu().numpy()[:, rows]
-    want_o, want_lse = oracle_rows(w, rank, rows, k_glob, v_glob)
+    del q, k, v, out, lse
+    if threaded:
+        want_o, want_lse = oracle_rows_threaded(w, rank, rows, k_glob, v_glob)
+    else:
+        want_o, want_lse = oracle_rows(w, rank, rows, k_glob, v_glob)
     stats = compare(w, out_rows, lse_rows, want_o, want_lse)
     print(f"[gpu]   -> {stats}", flush=True)
     return stats

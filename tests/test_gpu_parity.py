@@ -107,6 +107,17 @@ def test_bf16_full_size_sampled_rows(name, rows):
     check(w, stats)
 
 
+@pytest.mark.parametrize("name", ["128k-contiguous-causal", "1m-contiguous-causal"])
+def test_bf16_4096_sampled_rows_per_head(name):
+    """The large shares at the sample size their statement asks for: 4096
+    seeded query rows (0, 1 and b-1 among them) of every head, in the bench's
+    launch configuration; the oracle side runs in a thread pool."""
+    w = wl.WORKLOADS[name]
+    stats = run_and_compare(w, w.ranks[0], 4096, seed_rows=1, threaded=True)
+    assert stats["rows"] == 4096
+    check(w, stats)
+
+
 @pytest.mark.parametrize("name", ["32k-contiguous-causal", "32k-striped-causal", "32k-zigzag-causal"])
 def test_bf16_32k_every_row_of_two_heads(name):
     """Every query row of the first and the last query head (key/value heads 0

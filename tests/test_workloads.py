@@ -39,3 +39,20 @@ def test_sample_local_rows():
     assert np.all(np.diff(s) > 0)
     assert np.array_equal(s, wl.sample_local_rows(1000, 64, 5, 2))
     assert np.array_equal(wl.sample_local_rows(10, 64, 5, 0), np.arange(10))
+
+
+def test_threaded_oracle_rows_equal_plain_oracle_rows():
+    """The thread-pool evaluation used for large parity samples gives the plain
+    oracle's values (it only splits the rows)."""
+    import numpy as np
+
+    import parity_util as pu
+
+    w = wl.Workload("thr", N=2048, P=4, ranks=(3,), layout="striped", causal=True, Hq=4, Hkv=2, d=64,
+                    dtype="bf16", seed=5)
+    k_glob, v_glob = wl.global_kv(w)
+    rows = wl.sample_local_rows(w.b, 300, 5, 0)
+    o1, l1 = pu.oracle_rows(w, 3, rows, k_glob, v_glob)
+    o2, l2 = pu.oracle_rows_threaded(w, 3, rows, k_glob, v_glob, threads=3)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-13)
