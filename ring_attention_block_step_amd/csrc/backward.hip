@@ -225,6 +225,25 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const lds_t* l) {
 __device__ __forceinline__ void load_lds16(const unsigned char* g, lds_t* l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
+__device__ __forceinline__ uint32_t lds_addr(const lds_t* p) { return (uint32_t)(uintptr_t)p; }
+
+// 16-byte LDS read that the compiler's wait insertion does not track.  The
+// compiler's own waits for tracked reads in these loops drain the whole queue
+// (lgkmcnt(0)) where only the oldest read is needed; a pipeline that reads this
+// way waits for each operand itself with wait_lgkm_tied.  addr: per-lane LDS
+// byte address; off: a compile-time offset.
+template <int off, typename T>
+__device__ __forceinline__ void lds_read16_untracked(T& r, uint32_t addr) {
+  static_assert(sizeof(T) == 16 && off >= 0 && off < 65536, "ds_read_b128");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off) : "memory");
+}
+// s_waitcnt lgkmcnt(n), with r an in/out operand: whatever uses r cannot be
+// scheduled above the wait.
+template <int n, typename T>
+__device__ __forceinline__ void wait_lgkm_tied(T& r) {
+  static_assert(n >= 0 && n < 16, "lgkmcnt immediate");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(n));
+}
 
 // Fragment reads of an item tile (IT::QK or IT::DOK) held in LDS.
 template <int D>
@@ -682,26 +701,43 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsB[kk][e] = (__bf16)0.0f;
-#pragma unroll
-    for (int j = 0; j < kPF; ++j) fr[j] = tfrag(tbuf(0), 0, j / 2, j % 2);
+    // The pipeline's fragment reads are untracked: one read per MFMA, kPF
+    // MFMAs ahead, so before each MFMA exactly kPF-1 reads were issued after
+    // its operand.  Lane parts of the addresses (K, V tiles: row l32, chunk hi;
+    // K^T tiles: row l32, chunk hi); the rest is a compile-time offset.
+    const uint32_t lane_k = (uint32_t)key_tile_off(l32, hi);
+    const uint32_t lane_t = (uint32_t)val_tile_off<D>(l32, hi);
+    constexpr int TROW = D * 16;   // bytes per K^T chunk column
+    [&]<int... j>(std::integer_sequence<int, j...>) {
+      (lds_read16_untracked<(j % 2) * 2 * TROW + (j / 2) * 512>(fr[j], lds_addr(tbuf(0)) + lane_t), ...);
+    }(std::make_integer_sequence<int, kPF>{});
 
     // One half-tile block.  Block h = 2t + half: dQ of block h-1 from K^T of
     // (tp, hp) with dsp; S, dP of block h+1 from K, V of (tn, hn); VALU of
     // block h into dsc.  The fragments of the next block's first kPF groups
     // are K^T of (t, half) (the next block's dQ is dQ(h)).
-    auto block = [&](int t, int half, const bf16x8 (&dsp)[2], bf16x8 (&dsc)[2]) {
-      const int tp = half ? t : t - 1, hp = half ? 0 : 1;   // block h-1
-      const int tn = half ? t + 1 : t, hn = half ? 0 : 1;   // block h+1
-      const lds_t* tb_prev = tbuf(tp < 0 ? 0 : tp);
-      const lds_t* tb_cur = tbuf(t);
-      const lds_t* kb_next = kbuf(tn);
-      const lds_t* vb_next = vbuf(tn);
+    auto block = [&](int t, auto half_c, const bf16x8 (&dsp)[2], bf16x8 (&dsc)[2]) {
+      constexpr int half = decltype(half_c)::value;
+      constexpr int hp = half ? 0 : 1, hn = half ? 0 : 1;
+      const int tp = half ? t : t - 1;   // block h-1
+      const int tn = half ? t + 1 : t;   // block h+1
+      const uint32_t tb_prev = lds_addr(tbuf(tp < 0 ? 0 : tp)) + lane_t;
+      const uint32_t tb_cur = lds_addr(tbuf(t)) + lane_t;
+      const uint32_t kb_next = lds_addr(kbuf(tn)) + lane_k;
+      const uint32_t vb_next = lds_addr(vbuf(tn)) + lane_k;
       float pv[16], dsv[16];
-      auto frag = [&](int m) -> bf16x8 {
-        if (m < 2 * DT) return tfrag(tb_prev, hp, m / 2, m % 2);
-        if (m < 2 * DT + KS) return kfrag(kb_next, hn, m - 2 * DT);
-        if (m < NG) return kfrag(vb_next, hn, m - 2 * DT - KS);
-        return tfrag(tb_cur, half, (m - NG) / 2, (m - NG) % 2);
+      // Fragment m of this block's group sequence into ring slot m % kPF.
+      auto read_frag = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        bf16x8& f = fr[m % kPF];
+        if constexpr (m < 2 * DT)
+          lds_read16_untracked<(2 * hp + m % 2) * 2 * TROW + (m / 2) * 512>(f, tb_prev);
+        else if constexpr (m < 2 * DT + KS)
+          lds_read16_untracked<(m - 2 * DT) * 2048 + hn * 512>(f, kb_next);
+        else if constexpr (m < NG)
+          lds_read16_untracked<(m - 2 * DT - KS) * 2048 + hn * 512>(f, vb_next);
+        else
+          lds_read16_untracked<(2 * half + (m - NG) % 2) * 2 * TROW + ((m - NG) / 2) * 512>(f, tb_cur);
       };
       auto unit = [&](int e) {
         const float x = __builtin_amdgcn_exp2f(fmaf(s[e], a.sl2, -l2));
@@ -717,6 +753,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
       auto group = [&](auto mc) {
         constexpr int m = decltype(mc)::value;
         bf16x8& f = fr[m % kPF];
+        wait_lgkm_tied<kPF - 1>(f);
         if constexpr (m < 2 * DT) {
           o[m / 2] = mfma(f, dsp[m % 2], o[m / 2]);
           pin(o[m / 2]);
@@ -739,7 +776,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
           dp = mfma(f, df[ks], dp);
           pin(dp);
         }
-        f = frag(m + kPF);
+        read_frag(std::integral_constant<int, m + kPF>{});
         __builtin_amdgcn_sched_barrier(0);
       };
       [&]<int... ms>(std::integer_sequence<int, ms...>) { (group(std::integral_constant<int, ms>{}), ...); }
@@ -748,9 +785,9 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
 
     for (; t < F; ++t) {
       begin_iter(t);
-      block(t, 0, dsB, dsA);
-      block(t, 1, dsA, dsB);
-      wait_all_and_sync();
+      block(t, std::integral_constant<int, 0>{}, dsB, dsA);
+      block(t, std::integral_constant<int, 1>{}, dsA, dsB);
+      wait_all_and_sync();   // also drains the untracked reads
     }
     // dQ of the last fast block (tile F-1, half 1); the S, dP it formed for
     // tile F are discarded.
