@@ -18,6 +18,9 @@ striped and zigzag layouts, 32k and 128k shares), and
 ``backward_other_workloads`` the backward on the 128k share.
 ``reference_gemm`` times the vendor's dense bf16 GEMM on the same GPU (the
 practical dense-MFMA rate under sustained load, for context).
+``sclk_during_timed_region`` is the engine clock the driver reported while the
+timed steps ran, and ``pct_of_bf16_peak_at_measured_clock`` the rate against
+the peak scaled to that clock.
 ``merge_kernel`` and ``decode_kernel`` report the two HBM-bound kernels (the
 triple merge; the pass-Q decode partial of one resident shard) as achieved GB/s
 against 8 TB/s; ``backward`` reports the backward ring of a workload's rank as
@@ -405,6 +408,68 @@ def copy_calibration(nbytes: int, reps: int = 3) -> None:
 # Main.
 # ---------------------------------------------------------------------------
 
+class ClockSampler:
+    """The engine clock the kernel driver reports while the timed region runs:
+    a background thread reads the current level of pp_dpm_sclk in sysfs every
+    `period` seconds.  Used only when the box shows exactly one such file (one
+    GPU); otherwise, or on any read error, the summary is None."""
+
+    PUBLISHED_MHZ = 2400.0
+
+    def __init__(self, period: float = 0.01):
+        import glob
+
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    def _read(self):
+        import re
+
+        with open(self.paths[0]) as f:
+            for line in f:
+                m = re.search(r"(\d+)\s*Mhz\s*\*", line)
+                if m:
+                    return float(m.group(1))
+        return None
+
+    def __enter__(self):
+        import threading
+
+        if len(self.paths) != 1:
+            return self
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    v = self._read()
+                except OSError:
+                    return
+                if v is not None:
+                    self.samples.append(v)
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=1.0)
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = self.samples
+        return {"mean_mhz": sum(v) / len(v), "min_mhz": min(v), "max_mhz": max(v), "samples": len(v),
+                "source": self.paths[0] + " (current level)", "published_mhz": self.PUBLISHED_MHZ}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -486,13 +551,16 @@ def main(argv=None) -> int:
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    clock = ClockSampler()
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        run()
-    stop.record()
-    torch.cuda.synchronize()
+    with clock:
+        start.record()
+        for _ in range(args.steps):
+            run()
+        stop.record()
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = clock.summary()
     ra.timing_enable(False)
     kt = ra.timing_collect()
     ms_per_step = start.elapsed_time(stop) / args.steps
@@ -549,6 +617,9 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "N": w.N, "P": w.P, "b": w.b, "rank": rank, "layout": w.layout,
                    "causal": w.causal, "Hq": w.Hq, "Hkv": w.Hkv, "d_h": w.d, "useful_flops": flops},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "sclk_during_timed_region": sclk,
+        "pct_of_bf16_peak_at_measured_clock": (100.0 * value / (PEAK_BF16_TFLOPS * sclk["mean_mhz"] /
+                                                                 ClockSampler.PUBLISHED_MHZ)) if sclk else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity_sample": parity,

@@ -146,3 +146,27 @@ def test_shard_helpers_match_layout_definitions():
         packed = ra.pack_shards(x, P, layout)
         for r in range(P):
             assert torch.equal(packed[r], x[ra.shard_index(N, P, layout, r)])
+
+
+def test_bench_clock_sampler_reads_the_current_level(tmp_path):
+    """The bench's clock sampler takes the level marked '*' of a pp_dpm_sclk
+    file and summarises what it read while its block ran."""
+    import time
+
+    import bench
+
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("S: 1620Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    c = bench.ClockSampler(period=0.005)
+    c.paths = [str(f)]
+    with c:
+        time.sleep(0.05)
+    s = c.summary()
+    assert s is not None and s["mean_mhz"] == 1620.0 and s["samples"] >= 2
+    f.write_text("0: 500Mhz\n1: 2400Mhz *\n")
+    assert c._read() == 2400.0
+    none = bench.ClockSampler()
+    none.paths = []
+    with none:
+        pass
+    assert none.summary() is None
