@@ -218,6 +218,33 @@ def test_forward_on_side_stream_and_deterministic():
     assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
 
 
+def test_merge_at_the_bench_shape_sampled_rows():
+    """The merge at the shape the bench times (8 partials x 16384 rows x 32
+    heads x d 128, bf16 out), inputs drawn like the bench's (m ~ 4 N(0,1),
+    z ~ U(0.5, 1.5), y ~ N(0,1)) but seeded on the host; 512 sampled rows of
+    every head against the oracle merge."""
+    n, rows, Hq, d = 8, 16384, 32, 128
+    g = torch.Generator().manual_seed(707)
+    m = torch.randn(n, Hq, rows, generator=g) * 4
+    z = torch.rand(n, Hq, rows, generator=g) + 0.5
+    y = torch.randn(n, rows, Hq, d, generator=g)
+    out, lse = ra.merge(m.cuda(), z.cuda(), y.cuda(), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    sel = wl.sample_local_rows(rows, 512, 707, 0)
+    want_o, want_lse = oracle.merge_partials(m[:, :, sel].double().numpy().transpose(0, 2, 1),
+                                             z[:, :, sel].double().numpy().transpose(0, 2, 1),
+                                             y[:, sel].double().numpy())
+    got = out[torch.as_tensor(sel)].float().cpu().double().numpy()
+    err = np.abs(got - want_o)
+    got_lse = lse[:, torch.as_tensor(sel)].cpu().double().numpy().T
+    lerr = np.abs(got_lse - want_lse).max()
+    print(f"[gpu] merge 8x16384x32x128 bf16: O max-abs {err.max():.3e} (max |O| {np.abs(want_o).max():.3e}), "
+          f"LSE max-abs {lerr:.3e}", flush=True)
+    # bf16 output: one rounding of |O| (2^-9 relative) on top of fp32 arithmetic
+    assert (err <= 2.0 ** -8 * np.abs(want_o) + 1e-6).all()
+    assert lerr <= 1e-5
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("n,rows,Hq,d", [(8, 300, 4, 128), (3, 77, 2, 64), (1, 5, 1, 128)])
 def test_merge_matches_oracle(out_dtype, n, rows, Hq, d):
