@@ -23,7 +23,8 @@ timed steps ran, and ``pct_of_bf16_peak_at_measured_clock`` the rate against
 the peak scaled to that clock.
 ``merge_kernel`` and ``decode_kernel`` report the two HBM-bound kernels (the
 triple merge; the pass-Q decode partial of one resident shard) as achieved GB/s
-against 8 TB/s; ``backward`` reports the backward ring of a workload's rank as
+against 8 TB/s, the merge with the HBM bytes its counters measured
+(``traffic``); ``backward`` reports the backward ring of a workload's rank as
 useful TFLOP/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -48,6 +49,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2516.6     # 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_bf16_traffic.json")
+MERGE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "merge_traffic.json")
+MERGE_SOURCE = os.path.join(ROOT, "ring_attention_block_step_amd", "csrc", "merge.hip")
 STEP_SOURCE = os.path.join(ROOT, "ring_attention_block_step_amd", "csrc", "step_bf16.hip")
 
 
@@ -124,6 +127,20 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     if rec.get("workload") != workload or rec.get("step_source_sha256_16") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def measured_merge_traffic():
+    """HBM bytes per merge launch at the bench's merge shape from committed
+    rocprofv3 counter runs, or None when they are missing or were taken on a
+    different kernel source."""
+    try:
+        with open(MERGE_TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("shape") != dict(MERGE_SHAPE) or rec.get("merge_source_sha256_16") != source_digest(MERGE_SOURCE):
         return None
     return rec.get("bytes_per_launch")
 
@@ -229,7 +246,7 @@ def measure_merge(reps: int = 10) -> dict:
     gbs = nbytes / (avg_ms * 1e-3) / 1e9
     return {"kernel": "merge_kernel<128,bf16>", "shape": dict(MERGE_SHAPE), "bytes_per_launch": nbytes,
             "avg_launch_ms": avg_ms, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": gbs / PEAK_HBM_GBS, "launches": t["merge_launches"]}
+            "frac": gbs / PEAK_HBM_GBS, "launches": t["merge_launches"], "traffic": measured_merge_traffic()}
 
 
 BACKWARD_OTHER_WORKLOADS = ("128k-contiguous-causal",)

@@ -170,3 +170,13 @@ def test_bench_clock_sampler_reads_the_current_level(tmp_path):
     with none:
         pass
     assert none.summary() is None
+
+
+def test_bench_traffic_records_match_the_kernel_sources():
+    """The committed counter records that the bench reports as `traffic` were
+    taken on the current step and merge kernel sources (a changed kernel
+    needs a new counter run, and the bench then reports null)."""
+    import bench
+
+    assert bench.measured_traffic("1m-contiguous-causal") is not None
+    assert bench.measured_merge_traffic() is not None
