@@ -124,20 +124,38 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     *reinterpret_cast<uint4*>(blk + Item<D>::DOK + Item<D>::off(row, cc)) = dv;
   }
   // Stats: D = rowsum(dO * O) in fp32 from the bf16 values, LSE in log2 units.
-  if (threadIdx.x < 32) {
-    const int row = threadIdx.x, i = q0 + row;
-    float dsum = 0.f, l2 = INFINITY;
+  // Eight threads per row, each reading 16-byte chunks c = part, part + 8, ..
+  // of the row (coalesced across the row's threads), then a sum over the eight.
+  {
+    const int row = threadIdx.x >> 3, part = threadIdx.x & 7, i = q0 + row;
+    float dsum = 0.f;
     if (i < a.b) {
-      const uint16_t* o = reinterpret_cast<const uint16_t*>(a.out) + ((size_t)i * a.Hq + hq) * D;
-      const uint16_t* g = dout + ((size_t)i * a.Hq + hq) * D;
-      for (int c = 0; c < D; ++c)
-        dsum = fmaf(__uint_as_float((uint32_t)o[c] << 16), __uint_as_float((uint32_t)g[c] << 16), dsum);
-      const float lse = a.lse[(size_t)hq * a.b + i];
-      l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+      const uint4* o4 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.out) +
+                                                       ((size_t)i * a.Hq + hq) * D);
+      const uint4* g4 = reinterpret_cast<const uint4*>(dout + ((size_t)i * a.Hq + hq) * D);
+      for (int c = part; c < CPR; c += 8) {
+        const uint4 ov = o4[c], gv = g4[c];
+        const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dsum = fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(gw[e] << 16), dsum);
+          dsum = fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), dsum);
+        }
+      }
     }
-    float* st = reinterpret_cast<float*>(blk + Item<D>::STATS);
-    st[row] = l2;
-    st[32 + row] = dsum;
+    dsum += __shfl_xor(dsum, 1, 8);
+    dsum += __shfl_xor(dsum, 2, 8);
+    dsum += __shfl_xor(dsum, 4, 8);
+    if (part == 0) {
+      float l2 = INFINITY;
+      if (i < a.b) {
+        const float lse = a.lse[(size_t)hq * a.b + i];
+        l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+      }
+      float* st = reinterpret_cast<float*>(blk + Item<D>::STATS);
+      st[row] = l2;
+      st[32 + row] = dsum;
+    }
   }
 }
 
