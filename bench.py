@@ -613,7 +613,7 @@ def main(argv=None) -> int:
     gemm = None if args.no_gemm_ref else measure_reference_gemm()
     others = None if args.no_workloads else measure_workloads()
     decode = None if args.no_decode else measure_decode(args.decode_workload)
-    backward = None if args.no_backward else measure_backward(args.backward_workload)
+    backward = None if args.no_backward else measure_backward(args.backward_workload, reps=10)
     backward_other = None
     if not args.no_backward and not args.no_workloads:
         backward_other = [measure_backward(n, reps=2) for n in BACKWARD_OTHER_WORKLOADS if n != args.backward_workload]
