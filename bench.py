@@ -433,7 +433,7 @@ def copy_calibration(nbytes: int, reps: int = 3) -> None:
 class ClockSampler:
     """The engine clock the kernel driver reports while the timed region runs:
     a background thread reads the current level of pp_dpm_sclk in sysfs every
-    `period` seconds.  Used only when the box shows exactly one such file (one
+    `period` seconds.  Used only when the machine shows exactly one such file (one
     GPU); otherwise, or on any read error, the summary is None."""
 
     PUBLISHED_MHZ = 2400.0
