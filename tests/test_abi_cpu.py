@@ -77,6 +77,8 @@ def _fwd(fn, **kw):
     (dict(layout=2, N=1028), 1, "multiple of 2P"),
     (dict(d=96), 2, "d_h"),
     (dict(d=256), 2, "d_h"),
+    (dict(N=1 << 31, P=4, Hq=4, Hkv=2), 2, "too large"),
+    (dict(N=4 << 20, P=4, Hq=64, Hkv=8), 2, "too large"),
 ])
 def test_forward_rejects_bad_arguments(entry, kw, status, needle):
     L = _lib()
@@ -95,6 +97,8 @@ def test_merge_rejects_bad_arguments_and_accepts_empty():
     assert m(FAKE, FAKE, FAKE, 2, 10, 4, 128, FAKE, 2, None, None) == 1
     assert m(FAKE, FAKE, MISALIGNED, 2, 10, 4, 128, FAKE, 0, None, None) == 1
     assert m(FAKE, FAKE, FAKE, 2, 10, 4, 32, FAKE, 0, None, None) == 2
+    assert m(FAKE, FAKE, FAKE, 2, 1 << 29, 4, 128, FAKE, 0, None, None) == 2
+    assert "too many rows" in L.ringattn_last_error().decode()
     # zero rows: valid, nothing to do, no HIP call
     assert m(FAKE, FAKE, FAKE, 2, 0, 4, 128, FAKE, 0, None, None) == 0
 
@@ -115,6 +119,38 @@ def test_decode_rejects_bad_arguments():
     assert "Hq" in L.ringattn_last_error().decode()
     assert d(FAKE, FAKE, FAKE, 1, 10, 4, 1, 96, FAKE, FAKE, FAKE, None) == 2
     assert "d_h" in L.ringattn_last_error().decode()
+
+
+def test_backward_rejects_bad_arguments():
+    L = _lib()
+    f32 = ctypes.POINTER(ctypes.c_float)
+    fk = ctypes.cast(FAKE, f32)
+    fm = ctypes.cast(MISALIGNED, f32)
+
+    def bwd(**kw):
+        g = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=fk, dout=FAKE, dq=fk, dk=fk, dv=fk, N=1024, P=4, rank=0,
+                 Hq=4, Hkv=2, d=128, causal=1, layout=0)
+        g.update(kw)
+        return L.ringattn_backward(g["q"], g["k"], g["v"], g["out"], g["lse"], g["dout"], g["dq"], g["dk"],
+                                   g["dv"], g["N"], g["P"], g["rank"], g["Hq"], g["Hkv"], g["d"], g["causal"],
+                                   g["layout"], None)
+
+    for kw, status, needle in [
+        (dict(lse=None), 1, "non-null"),
+        (dict(dout=None), 1, "non-null"),
+        (dict(dk=None), 1, "non-null"),
+        (dict(dq=fm), 1, "aligned"),
+        (dict(dout=MISALIGNED), 1, "aligned"),
+        (dict(q=None), 1, "non-null"),
+        (dict(P=0), 1, "P must be"),
+        (dict(rank=4), 1, "rank"),
+        (dict(Hq=3), 1, "Hq"),
+        (dict(layout=2, N=1028), 1, "multiple of 2P"),
+        (dict(d=96), 2, "d_h"),
+        (dict(N=1 << 31), 2, "too large"),
+    ]:
+        assert bwd(**kw) == status, kw
+        assert needle in L.ringattn_last_error().decode(), (kw, L.ringattn_last_error())
 
 
 def test_timing_collect_empty():
