@@ -70,6 +70,8 @@ enum { RINGATTN_LAYOUT_CONTIGUOUS = 0, RINGATTN_LAYOUT_STRIPED = 1, RINGATTN_LAY
  *  d_h                      64 or 128
  *  causal                   0 or 1
  *  layout                   RINGATTN_LAYOUT_CONTIGUOUS, _STRIPED or _ZIGZAG
+ *  Limits: b <= 2^28 and Hq * b <= 2^25 (the kernels index rows in 32 bits);
+ *  a larger shard returns RINGATTN_EUNSUPPORTED.
  *
  * The library allocates its workspace (two key/value slots and the fp32 running
  * state) stream-ordered on `stream` and frees it the same way.  The block for
@@ -108,8 +110,8 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
  *                                rank never sees get nothing).  Zero them
  *                                before the first rank; after all P ranks
  *                                they hold the full gradients.
- *  N, P, rank, Hq, Hkv, d_h, causal, layout as for ringattn_forward.
- *  Every pointer is required and 16-byte aligned.
+ *  N, P, rank, Hq, Hkv, d_h, causal, layout as for ringattn_forward, with
+ *  the same limits.  Every pointer is required and 16-byte aligned.
  *
  * The library allocates its workspace (the query rows' packed tiles and two
  * packed key/value slots) stream-ordered on `stream`; the slot of visit s+1 is
@@ -133,7 +135,8 @@ int ringattn_backward(const void* q, const void* k, const void* v, const void* o
  *  lse   [Hq, rows]               fp32 (written), may be NULL
  *  A partial with m = -inf, z = 0 contributes nothing; a row whose partials
  *  are all empty gets O = 0 and LSE = -inf.  nparts >= 1, rows >= 0, Hq >= 1,
- *  d_h in {64, 128}.
+ *  d_h in {64, 128}; rows * Hq <= 2^30, else RINGATTN_EUNSUPPORTED.  rows = 0
+ *  is valid and enqueues nothing.
  */
 int ringattn_merge(const float* m, const float* z, const float* y, int nparts,
                    int64_t rows, int Hq, int d_h, void* out, int out_dtype,
@@ -157,7 +160,9 @@ int ringattn_merge(const float* m, const float* z, const float* y, int nparts,
  *  m, z     [Hq, n_q]           fp32 (written): m in natural-log units
  *  y        [n_q, Hq, d_h]      fp32, unnormalised (written)
  *  n_q >= 1, n_keys >= 0, Hq % Hkv == 0, d_h in {64, 128}.  q, k, v and y
- *  must be 16-byte aligned, m and z 4-byte aligned.
+ *  must be 16-byte aligned, m and z 4-byte aligned.  Limits: Hq * n_q <= 2^30,
+ *  (Hq / Hkv) * n_q <= 16 * 65535 and ceil(n_keys / 256) <= 2^30, else
+ *  RINGATTN_EUNSUPPORTED.
  *
  * These are exactly one part of ringattn_merge's inputs: pointing m, z, y at
  * part p of arrays [P, Hq, n_q] and [P, n_q, Hq, d_h] and then calling

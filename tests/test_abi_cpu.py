@@ -119,6 +119,8 @@ def test_decode_rejects_bad_arguments():
     assert "Hq" in L.ringattn_last_error().decode()
     assert d(FAKE, FAKE, FAKE, 1, 10, 4, 1, 96, FAKE, FAKE, FAKE, None) == 2
     assert "d_h" in L.ringattn_last_error().decode()
+    assert d(FAKE, FAKE, FAKE, 1 << 20, 10, 1, 1, 128, FAKE, FAKE, FAKE, None) == 2
+    assert "too large" in L.ringattn_last_error().decode()
 
 
 def test_backward_rejects_bad_arguments():
