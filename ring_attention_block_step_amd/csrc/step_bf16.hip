@@ -51,6 +51,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_t;
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_t* p) { return (uint32_t)(uintptr_t)p; }
@@ -346,6 +347,22 @@ __device__ __forceinline__ void wait_keep_and_sync() {
 // A probability above this (or a NaN) sends the workgroup to the exact kernel.
 constexpr float kSafeSum = 16777216.0f;  // 2^24, bound on a lane's 16 probabilities per half tile
 
+__device__ __forceinline__ int wave_of_thread() { return (int)(threadIdx.x >> 6); }
+
+// Direct global -> LDS copy of 16 bytes per lane to the wave-uniform address
+// l + 16 * lane.  A device function: the host pass of a kernel template that
+// names the builtin itself drops the kernel's launch stub.
+__device__ __forceinline__ void stage16(const float* g, lds_t* l) { __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0); }
+
+// Offset (floats) of register r of subtile (nt, dt), lane `lane`, in one
+// item's carried y: four consecutive registers of a lane are contiguous, so a
+// wave moves 1 KB per float4 access and a direct-to-LDS copy of a subtile
+// lands where ds_read_b128 of lane `lane` finds its four registers.
+template <int DT>
+__device__ __forceinline__ int carry_off(int nt, int dt, int r4, int lane) {
+  return (((nt * DT + dt) * 4 + r4) * 64 + lane) * 4;
+}
+
 template <int D, int NT, bool EXACT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512 / NT, 512 / NT), amdgpu_waves_per_eu(3 - NT, 3 - NT)))
 void step_bf16_kernel(StepBf16Args a) {
@@ -363,8 +380,11 @@ void step_bf16_kernel(StepBf16Args a) {
   // every load has a whole iteration to land before it is waited for.  (A
   // fourth value buffer would let the barrier skip its LDS drain, but the
   // larger footprint measured a third of the L2 reuse between workgroups.)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[7 * S::TILE];
+  // Behind them, 4 KB per wave stage the carried y of one 32-row subtile
+  // (see the late fold below).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[7 * S::TILE + WAVES * 4096];
   lds_t* smem = (lds_t*)(smem_raw);
+  lds_t* ystage = smem + 7 * S::TILE + wave_of_thread() * 4096;
   auto kbuf = [smem](int t) { return smem + (t & 3) * S::TILE; };
   auto vbuf = [smem](int t) { return smem + (4 + t % 3) * S::TILE; };
 
@@ -419,29 +439,55 @@ void step_bf16_kernel(StepBf16Args a) {
   float mref[NT], zs[NT];
   const size_t ig = (size_t)hq * a.npb + pblk;
   const size_t ystride = (size_t)(NT * DT * 16 * 64);
+  // Late fold: the fast pipeline keeps the carried m as its fixed reference,
+  // so y may start from zero and the carried y be added at any point of the
+  // pipeline with no rescale.  Subtile j is copied global -> LDS at the top
+  // of iteration j (completed by that iteration's closing wait) and added at
+  // the top of iteration j + 1.  This spreads the 128 KB per workgroup over
+  // the first iterations instead of loading it with the first tiles, when
+  // every workgroup of a round loads at once.  Workgroups with fewer fast
+  // tiles, and the exact kernel, load y up front.
+  constexpr int NSL = NT * DT;
+  // (wave-uniform: taken through an SGPR so that every branch on it is scalar)
+  const bool fold_late =
+      __builtin_amdgcn_readfirstlane((int)(!EXACT && a.carry_in && active && F >= NSL + 1)) != 0;
+  const float* cyin = a.cy + ig * ystride;
+  // y starts at zero on every path (no load may be pending on it where the
+  // paths join), then the up-front path overwrites it.
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nt][dt][r] = 0.f;
   if (a.carry_in && active) {
-    const float* cy = a.cy + ig * ystride;
     const float* cm = a.cm + ig * (NT * 64);
     const float* cz = a.cz + ig * (NT * 64);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       mref[nt] = cm[nt * 64 + lane];
       zs[nt] = cz[nt * 64 + lane];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[nt][dt][r] = cy[((nt * DT + dt) * 16 + r) * 64 + lane];
     }
   } else {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       mref[nt] = -INFINITY;
       zs[nt] = 0.f;
+    }
+  }
+  if (a.carry_in && active && !fold_late) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[nt][dt][r] = 0.f;
-    }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 y4 = *reinterpret_cast<const float4*>(cyin + carry_off<DT>(nt, dt, r4, lane));
+          o[nt][dt][4 * r4 + 0] = y4.x;
+          o[nt][dt][4 * r4 + 1] = y4.y;
+          o[nt][dt][4 * r4 + 2] = y4.z;
+          o[nt][dt][4 * r4 + 3] = y4.w;
+        }
   }
 
   // Key/value tiles of this head: bpad / 64 per head in the slot.
@@ -515,6 +561,29 @@ void step_bf16_kernel(StepBf16Args a) {
   // pending inside the loop (its waits would drain the untracked ones too).
   if (F > 0) __builtin_amdgcn_s_waitcnt(0);
   for (; t < F; ++t) {
+    if (fold_late && t <= NSL) {
+      if (t >= 1) {
+#pragma unroll
+        for (int j = 0; j < NSL; ++j)
+          if (j == t - 1) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              f32x4 y4;
+              asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                           : "=v"(y4)
+                           : "v"(lds_addr(ystage) + (uint32_t)(r4 * 1024 + lane * 16))
+                           : "memory");
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[j / DT][j % DT][4 * r4 + e] += y4[e];
+            }
+          }
+      }
+      if (t < NSL) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          stage16(cyin + carry_off<DT>(t / DT, t % DT, r4, lane), ystage + r4 * 1024);
+      }
+    }
     float zt[NT];
     // Prefetches are unconditional so the loop body is one basic block; past
     // the last tile they fill a buffer no later iteration reads (V(t+2)
@@ -621,7 +690,9 @@ void step_bf16_kernel(StepBf16Args a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cy[((nt * DT + dt) * 16 + r) * 64 + lane] = o[nt][dt][r];
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<float4*>(cy + carry_off<DT>(nt, dt, r4, lane)) =
+              make_float4(o[nt][dt][4 * r4], o[nt][dt][4 * r4 + 1], o[nt][dt][4 * r4 + 2], o[nt][dt][4 * r4 + 3]);
     }
   }
 }
