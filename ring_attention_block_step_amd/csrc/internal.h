@@ -39,7 +39,7 @@ struct StepBf16Args {
   const __bf16* q;   // [b, Hq, D] caller's query rows
   const __bf16* kp;  // slot keys   [Hkv][bpad/64] tiles of 64 x D, chunk-major (key_tile_off)
   const __bf16* vp;  // slot values [Hkv][bpad/64] tiles of D x 64, transposed, chunk-major (val_tile_off)
-  const float* cy;   // running y in  [Hq*npb][kStepNT][D/32][16][64]  (register order)
+  const float* cy;   // running y in  [Hq*npb][kStepNT][D/32][4][64][4]: subtile, register/4, lane, register%4
   const float* cm;   // running m in  [Hq*npb][kStepNT][64]  (log2 units, scaled)
   const float* cz;   // running z in  [Hq*npb][kStepNT][64]  (per-lane partial sums)
   float* cyo;        // running state out, same layouts (never the input buffers)
