@@ -310,19 +310,15 @@ int ringattn_forward(const void* q, const void* k, const void* v, void* out, flo
   a.items = G * npb;
   a.wgs_per_head = (a.items + kStepWaves - 1) / kStepWaves;
   a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
-  const int grid = step_bf16_grid(a);
-  // extra: running state A, running state B (steps alternate), flags.
-  const size_t flag_bytes = round_up((size_t)grid * sizeof(int), 256);
-  const size_t extra_bytes = 2 * carry_bytes + flag_bytes;
+  // extra: running state A, running state B (steps alternate).
+  const size_t extra_bytes = 2 * carry_bytes;
 
   auto hop = [&](int r, char* slot, hipStream_t s) -> hipError_t {
     __bf16* kp = reinterpret_cast<__bf16*>(slot);
     return launch_pack_bf16(kb + (size_t)r * shard_elems, vb + (size_t)r * shard_elems, kp, kp + kv_elems, b,
                             bpad, Hkv, D, s);
   };
-  auto init = [&](char* extra, hipStream_t s) -> hipError_t {
-    return launch_zero_flags(reinterpret_cast<int*>(extra + 2 * carry_bytes), grid, s);
-  };
+  auto init = [&](char*, hipStream_t) -> hipError_t { return hipSuccess; };
   auto step = [&](char* slot, char* extra, int i, int, const BlockMask& mk, bool carry_in, bool last,
                   hipStream_t s) -> hipError_t {
     StepBf16Args x = a;
@@ -336,7 +332,6 @@ int ringattn_forward(const void* q, const void* k, const void* v, void* out, flo
     x.cyo = reinterpret_cast<float*>(cout);
     x.cmo = reinterpret_cast<float*>(cout + cy_bytes);
     x.czo = reinterpret_cast<float*>(cout + cy_bytes + cmz_bytes);
-    x.flags = reinterpret_cast<int*>(extra + 2 * carry_bytes);
     x.shift = mk.shift;
     x.kend = mk.kend;
     x.qbeg = mk.qbeg;

@@ -45,7 +45,6 @@ struct StepBf16Args {
   float* cyo;        // running state out, same layouts (never the input buffers)
   float* cmo;
   float* czo;
-  int* flags;        // [gridDim.x] set by the fast kernel for a workgroup that must be redone exactly
   __bf16* out;       // [b, Hq, D]
   float* lse;        // [Hq, b] or null
   int b, bpad, npb, Hq, Hkv, G;
@@ -145,11 +144,10 @@ inline int64_t padded_rows(int64_t b) { return (b + kKeyTile - 1) / kKeyTile * k
 hipError_t launch_pack_bf16(const __bf16* k_shard, const __bf16* v_shard, __bf16* kp, __bf16* vp,
                             int b, int bpad, int Hkv, int D, hipStream_t st);
 
-// The step as two launches: the fast kernel (fixed softmax reference per row,
-// flags workgroups whose probabilities would leave the safe range), then the
-// exact kernel, which returns at once unless its workgroup is flagged.
+// The step as one launch: a fixed softmax reference per row over the tiles the
+// workgroup sees in full, redone on the exact path by a workgroup whose
+// probabilities would leave the safe range.
 hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st);
-hipError_t launch_zero_flags(int* flags, int n, hipStream_t st);
 int step_bf16_grid(const StepBf16Args& a);
 hipError_t launch_step_f32(const StepF32Args& a, int D, hipStream_t st);
 hipError_t launch_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows,

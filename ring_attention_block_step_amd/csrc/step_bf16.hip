@@ -31,15 +31,15 @@
 // without the pipeline.
 //
 // Softmax in base 2: scores are scaled by log2(e)/sqrt(d) inside one FMA, and
-// m is kept in those units.  The fast kernel keeps one reference m per row for
-// the whole launch (the carried one, or the maximum of the row's first half
+// m is kept in those units.  The fast pipeline keeps one reference m per row
+// for all its tiles (the carried one, or the maximum of the row's first half
 // tile): any common reference cancels in y / z, so this is the same exact
 // recurrence with the rescale factor exp(m_old - m_new) applied to the
 // reference-free sums.  When a lane's 16 probabilities of a half tile sum to
-// more than 2^24 (or to a NaN) the workgroup is flagged, and the exact kernel
-// launched after it recomputes that workgroup from the untouched input state
-// with the running maximum, raising the reference when a maximum exceeds it
-// by more than 8 (a factor 2^8) and rescaling y and z by exp2(m_old - m_new).
+// more than 2^24 (or to a NaN) the workgroup starts over from its untouched
+// input state and takes every tile through the exact per-tile path, with the
+// running maximum, raising the reference when a maximum exceeds it by more
+// than 8 (a factor 2^8) and rescaling y and z by exp2(m_old - m_new).
 #include <utility>
 
 #include "internal.h"
@@ -344,7 +344,7 @@ __device__ __forceinline__ void wait_keep_and_sync() {
   asm volatile("" ::: "memory");
 }
 
-// A probability above this (or a NaN) sends the workgroup to the exact kernel.
+// A probability above this (or a NaN) sends the workgroup back to the exact path.
 constexpr float kSafeSum = 16777216.0f;  // 2^24, bound on a lane's 16 probabilities per half tile
 
 __device__ __forceinline__ int wave_of_thread() { return (int)(threadIdx.x >> 6); }
@@ -363,7 +363,7 @@ __device__ __forceinline__ int carry_off(int nt, int dt, int r4, int lane) {
   return (((nt * DT + dt) * 4 + r4) * 64 + lane) * 4;
 }
 
-template <int D, int NT, bool EXACT>
+template <int D, int NT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512 / NT, 512 / NT), amdgpu_waves_per_eu(3 - NT, 3 - NT)))
 void step_bf16_kernel(StepBf16Args a) {
   using S = Step<D, NT>;
@@ -372,8 +372,6 @@ void step_bf16_kernel(StepBf16Args a) {
   constexpr int DT = S::DT;
   constexpr int KS = S::KS;
 
-  // The exact kernel only redoes workgroups the fast kernel flagged.
-  if (EXACT && a.flags[blockIdx.x] == 0) return;
 
   // Four key buffers (tile t in t % 4) and three value buffers (t % 3):
   // iteration t reads K(t), K(t+1), V(t) while V(t+2) and K(t+3) stream in, so
@@ -385,6 +383,7 @@ void step_bf16_kernel(StepBf16Args a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[7 * S::TILE + WAVES * 4096];
   lds_t* smem = (lds_t*)(smem_raw);
   lds_t* ystage = smem + 7 * S::TILE + wave_of_thread() * 4096;
+  __shared__ int redo;  // set by any wave whose fast pass must be redone exactly
   auto kbuf = [smem](int t) { return smem + (t & 3) * S::TILE; };
   auto vbuf = [smem](int t) { return smem + (4 + t % 3) * S::TILE; };
 
@@ -417,9 +416,8 @@ void step_bf16_kernel(StepBf16Args a) {
   const int first_item = wgi * WAVES;
   const int last_item = min(first_item + WAVES - 1, a.items - 1);
   const int T = (keys_upto(min((last_item / a.G) * ROWS + ROWS, a.b)) + kKeyTile - 1) / kKeyTile;
-  // Tiles every row of the workgroup sees in full run in the fast pipeline;
-  // the exact kernel takes every tile through the per-tile path.
-  const int F = EXACT ? 0 : min(T, full_upto((first_item / a.G) * ROWS) / kKeyTile);
+  // Tiles every row of the workgroup sees in full run in the fast pipeline.
+  const int F = min(T, full_upto((first_item / a.G) * ROWS) / kKeyTile);
   const int my_tiles = active ? (keys_upto(min(q0 + ROWS, a.b)) + kKeyTile - 1) / kKeyTile : 0;
   const int my_full = full_upto(q0) / kKeyTile;
 
@@ -446,14 +444,15 @@ void step_bf16_kernel(StepBf16Args a) {
   // the top of iteration j + 1.  This spreads the 128 KB per workgroup over
   // the first iterations instead of loading it with the first tiles, when
   // every workgroup of a round loads at once.  Workgroups with fewer fast
-  // tiles, and the exact kernel, load y up front.
+  // tiles, and a workgroup sent back to the exact path, load y up front.
   constexpr int NSL = NT * DT;
   // (wave-uniform: taken through an SGPR so that every branch on it is scalar)
   const bool fold_late =
-      __builtin_amdgcn_readfirstlane((int)(!EXACT && a.carry_in && active && F >= NSL + 1)) != 0;
+      __builtin_amdgcn_readfirstlane((int)(a.carry_in && active && F >= NSL + 1)) != 0;
   const float* cyin = a.cy + ig * ystride;
   // y starts at zero on every path (no load may be pending on it where the
   // paths join), then the up-front path overwrites it.
+  auto load_state = [&](bool late) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -475,7 +474,7 @@ void step_bf16_kernel(StepBf16Args a) {
       zs[nt] = 0.f;
     }
   }
-  if (a.carry_in && active && !fold_late) {
+  if (a.carry_in && active && !late) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -489,6 +488,8 @@ void step_bf16_kernel(StepBf16Args a) {
           o[nt][dt][4 * r4 + 3] = y4.w;
         }
   }
+  };
+  load_state(fold_late);
 
   // Key/value tiles of this head: bpad / 64 per head in the slot.
   const size_t head_tiles = (size_t)(a.bpad / kKeyTile);
@@ -507,7 +508,7 @@ void step_bf16_kernel(StepBf16Args a) {
   for (int i = 0; i < 3 && i < T; ++i) issue_k(i);
   for (int i = 0; i < 2 && i < T; ++i) issue_v(i);
   wait_all_and_sync();
-  if (EXACT && tid == 0) a.flags[blockIdx.x] = 0;  // every thread has read the flag
+  if (tid == 0) redo = 0;  // ordered before any wave's vote by the fast loop's barriers
 
   f32x16 sa[NT], sb[NT];
   float mxa[NT];
@@ -621,11 +622,25 @@ void step_bf16_kernel(StepBf16Args a) {
     __builtin_amdgcn_s_waitcnt(0);
     S::pv_f(o, vf, p1);  // PV(F-1, 1)
   }
-  if (!EXACT && __builtin_amdgcn_ballot_w64(!ok) && lane == 0) a.flags[blockIdx.x] = 1;
+  // A wave whose fixed reference let a probability leave the safe range (or
+  // produced a NaN) sends the whole workgroup back to its first tile, with the
+  // state reloaded up front and every tile on the exact path below.  The
+  // carried state is only written at the end, so the input is untouched.
+  if (F > 0) {
+    if (__builtin_amdgcn_ballot_w64(!ok) && lane == 0) redo = 1;
+    wait_all_and_sync();
+    if (redo) {
+      load_state(false);
+      t = 0;
+      for (int i = 0; i < 3 && i < T; ++i) issue_k(i);
+      for (int i = 0; i < 2 && i < T; ++i) issue_v(i);
+      wait_all_and_sync();
+    }
+  }
 
   // Remaining tiles, with the exact running-maximum recurrence: element masks
   // (causal diagonal, ragged tail), waves whose rows end earlier than the
-  // workgroup's, and every tile of the exact kernel.
+  // workgroup's, and every tile of a workgroup sent back above.
   for (; t < T; ++t) {
     if (t + 2 < T) issue_v(t + 2);
     if (t + 3 < T) issue_k(t + 3);
@@ -697,11 +712,6 @@ void step_bf16_kernel(StepBf16Args a) {
   }
 }
 
-__global__ void zero_flags_kernel(int* flags, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) flags[i] = 0;
-}
-
 }  // namespace
 
 int step_bf16_grid(const StepBf16Args& a) { return a.wgs_per_head * a.Hkv; }
@@ -709,19 +719,10 @@ int step_bf16_grid(const StepBf16Args& a) { return a.wgs_per_head * a.Hkv; }
 hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st) {
   const dim3 grid((unsigned)step_bf16_grid(a));
   const dim3 block(64 * kStepWaves);
-  if (D == 128) {
-    hipLaunchKernelGGL((step_bf16_kernel<128, kStepNT, false>), grid, block, 0, st, a);
-    hipLaunchKernelGGL((step_bf16_kernel<128, kStepNT, true>), grid, block, 0, st, a);
-  } else {
-    hipLaunchKernelGGL((step_bf16_kernel<64, kStepNT, false>), grid, block, 0, st, a);
-    hipLaunchKernelGGL((step_bf16_kernel<64, kStepNT, true>), grid, block, 0, st, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_flags(int* flags, int n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_flags_kernel, dim3((n + 255) / 256), dim3(256), 0, st, flags, n);
+  if (D == 128)
+    hipLaunchKernelGGL((step_bf16_kernel<128, kStepNT>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((step_bf16_kernel<64, kStepNT>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -175,7 +175,7 @@ def test_late_dominant_key(layout, boost):
     vq = ra.pack_shards(v_glob, P, layout).cuda()
     for rank in range(P):
         q = q_glob[ra.shard_index(N, P, layout, rank)].cuda()
-        for _ in range(2):   # the second call must not see stale flags
+        for _ in range(2):   # a redo in one call leaves nothing behind for the next
             out, lse = ra.forward(q, kq, vq, P=P, rank=rank, causal=True, layout=layout)
         torch.cuda.synchronize()
         tq = oracle.shard_positions(layout, rank, P, b)
