@@ -204,6 +204,21 @@ int ringattn_timing_collect_backward(double* step_ms, int64_t* step_launches);
 int ringattn_timing_collect_decode(double* decode_ms, int64_t* decode_calls);
 
 /*
+ * Diagnostics of the bf16 step kernel's rescale schedule.  Its fast pipeline
+ * keeps one fixed softmax reference per row; a workgroup whose probabilities
+ * would leave the safe range against it (a later score far above the
+ * reference: "Ring Attention" (aarnphm.xyz), the rescale factor
+ * exp(m_old - m_new) of the recurrence for m, z, y) starts over on the exact
+ * path with the running maximum.  This call waits for all work on the current
+ * device, then writes the number of step-kernel workgroups that did so since
+ * the previous call (redone) and how many of those had been folding the
+ * carried running state in late (redone_late_fold), and clears both counts.
+ * Either pointer may be NULL.  The counts are per device and shared by every
+ * caller on it.
+ */
+int ringattn_redo_count(int64_t* redone, int64_t* redone_late_fold);
+
+/*
  * Debug switch: when serial = 1 every key/value hop copy runs on the caller's
  * stream instead of the library's second stream (no overlap).  Results are
  * bit-identical either way; used to test the double buffer for races.

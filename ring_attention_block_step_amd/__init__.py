@@ -21,8 +21,8 @@ import os
 import torch
 
 __all__ = ["forward", "backward", "merge", "decode_partial", "shard_index", "pack_shards", "lib", "RingAttnError",
-           "timing_enable", "timing_collect", "timing_collect_decode", "timing_collect_backward", "set_serial_hops", "version", "SYMBOLS",
-           "LIB_PATH"]
+           "timing_enable", "timing_collect", "timing_collect_decode", "timing_collect_backward", "set_serial_hops",
+           "redo_count", "version", "SYMBOLS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
 LAYOUTS = {"contiguous": 0, "striped": 1, "zigzag": 2}
@@ -31,7 +31,7 @@ LAYOUTS = {"contiguous": 0, "striped": 1, "zigzag": 2}
 SYMBOLS = ("ringattn_forward", "ringattn_forward_f32", "ringattn_backward", "ringattn_merge",
            "ringattn_decode_partial", "ringattn_status_string", "ringattn_last_error", "ringattn_timing_enable",
            "ringattn_timing_collect", "ringattn_timing_collect_backward", "ringattn_timing_collect_decode",
-           "ringattn_set_serial_hops", "ringattn_version")
+           "ringattn_redo_count", "ringattn_set_serial_hops", "ringattn_version")
 
 _lib = None
 
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.ringattn_timing_collect.restype = i32
     L.ringattn_timing_collect_decode.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.ringattn_timing_collect_decode.restype = i32
+    L.ringattn_redo_count.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    L.ringattn_redo_count.restype = i32
     L.ringattn_set_serial_hops.argtypes = [i32]
     L.ringattn_set_serial_hops.restype = i32
     L.ringattn_version.argtypes = []
@@ -309,6 +311,15 @@ def timing_collect_decode() -> dict:
     ms, n = ctypes.c_double(), ctypes.c_int64()
     _check(lib().ringattn_timing_collect_decode(ctypes.byref(ms), ctypes.byref(n)))
     return {"decode_ms": ms.value, "decode_calls": n.value}
+
+
+def redo_count() -> dict:
+    """Step-kernel workgroups that redid their tiles on the exact path since the
+    last call (all of them, and those that had been folding the carried state
+    in late); waits for the current device and clears the counts."""
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ringattn_redo_count(ctypes.byref(a), ctypes.byref(b)))
+    return {"redone": a.value, "redone_late_fold": b.value}
 
 
 def set_serial_hops(flag: bool) -> None:

@@ -568,6 +568,14 @@ int ringattn_timing_collect_decode(double* decode_ms, int64_t* decode_calls) {
   return status;
 }
 
+int ringattn_redo_count(int64_t* redone, int64_t* redone_late_fold) {
+  unsigned long long c[2] = {0ull, 0ull};
+  HIP_TRY(take_step_bf16_redo_counts(c));
+  if (redone) *redone = (int64_t)c[0];
+  if (redone_late_fold) *redone_late_fold = (int64_t)c[1];
+  return RINGATTN_OK;
+}
+
 int ringattn_set_serial_hops(int serial) {
   g_serial_hops = serial != 0;
   return RINGATTN_OK;

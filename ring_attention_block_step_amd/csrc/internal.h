@@ -149,6 +149,10 @@ hipError_t launch_pack_bf16(const __bf16* k_shard, const __bf16* v_shard, __bf16
 // probabilities would leave the safe range.
 hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st);
 int step_bf16_grid(const StepBf16Args& a);
+// Waits for the current device, then returns and clears its counts of step
+// kernel workgroups that redid their tiles exactly: [0] all, [1] those whose
+// fast pass folded the carried y in late.
+hipError_t take_step_bf16_redo_counts(unsigned long long counts[2]);
 hipError_t launch_step_f32(const StepF32Args& a, int D, hipStream_t st);
 hipError_t launch_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows,
                         int Hq, int D, void* out, int out_f32, float* lse, hipStream_t st);

@@ -347,6 +347,16 @@ __device__ __forceinline__ void wait_keep_and_sync() {
 // A probability above this (or a NaN) sends the workgroup back to the exact path.
 constexpr float kSafeSum = 16777216.0f;  // 2^24, bound on a lane's 16 probabilities per half tile
 
+}  // namespace
+
+// Workgroups of the step kernel that redid their tiles on the exact path,
+// counted on each device: [0] every such workgroup, [1] those among them whose
+// fast pass had been folding the carried y in late.  Read and cleared by
+// take_step_bf16_redo_counts().
+__device__ unsigned long long g_step_redo_counts[2];
+
+namespace {
+
 __device__ __forceinline__ int wave_of_thread() { return (int)(threadIdx.x >> 6); }
 
 // Direct global -> LDS copy of 16 bytes per lane to the wave-uniform address
@@ -630,6 +640,10 @@ void step_bf16_kernel(StepBf16Args a) {
     if (__builtin_amdgcn_ballot_w64(!ok) && lane == 0) redo = 1;
     wait_all_and_sync();
     if (redo) {
+      if (tid == 0) {
+        atomicAdd(&g_step_redo_counts[0], 1ull);
+        if (fold_late) atomicAdd(&g_step_redo_counts[1], 1ull);
+      }
       load_state(false);
       t = 0;
       for (int i = 0; i < 3 && i < T; ++i) issue_k(i);
@@ -715,6 +729,16 @@ void step_bf16_kernel(StepBf16Args a) {
 }  // namespace
 
 int step_bf16_grid(const StepBf16Args& a) { return a.wgs_per_head * a.Hkv; }
+
+hipError_t take_step_bf16_redo_counts(unsigned long long counts[2]) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbol(counts, HIP_SYMBOL(g_step_redo_counts), 2 * sizeof(unsigned long long), 0,
+                          hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  const unsigned long long zero[2] = {0ull, 0ull};
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_step_redo_counts), zero, sizeof zero, 0, hipMemcpyHostToDevice);
+}
 
 hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st) {
   const dim3 grid((unsigned)step_bf16_grid(a));

@@ -18,18 +18,22 @@ import ring_attention_block_step_amd as ra
 import workloads as wl
 
 # Bounds.  fp32: max-abs <= 1e-5 on O.  bf16 inputs with fp32 accumulation:
-# max-abs <= 1e-2 and mean-abs <= 1e-3 on O, the stated bounds, with one
-# allowance for the bf16 OUTPUT format itself: an element with |O| >= 1.28 may
-# differ by 2^-7 |O| (one bf16 ulp; the half-ulp of the output alone exceeds
-# 1e-2 once |O| >= 4), and the mean bound adds the mean output rounding,
-# 2^-9 mean|O|.  On the named workloads mean|O| is ~1e-2, so the mean bound is
-# the stated one to within 5e-5; the allowances matter only for rows that see a
-# handful of keys.  LSE bounds are not stated; these are adopted here.
+# max-abs <= 1e-2 and mean-abs <= 1e-3 on O, the stated bounds.  The named
+# full-size workloads are held to exactly these (check(..., allowance=False)).
+# The small edge-case shapes get one allowance for the bf16 OUTPUT format
+# itself: an element with |O| >= 1.28 may differ by 2^-7 |O| (one bf16 ulp;
+# the half-ulp of the output alone exceeds 1e-2 once |O| >= 4), and the mean
+# bound adds the mean output rounding, 2^-9 mean|O|.  Rows that see a handful
+# of keys (tiny shards, the first striped rows) reach such |O|.  The elements
+# that need the allowance are counted, printed and bounded by
+# ALLOWANCE_FRACTION of the case.  LSE bounds are not stated; these are
+# adopted here.
 TOL = {
     "f32": {"max_abs": 1e-5, "lse_max_abs": 1e-5},
     "bf16": {"max_abs": 1e-2, "mean_abs": 1e-3, "lse_max_abs": 1e-3, "rel_ulp": 2.0 ** -7,
              "mean_rel": 2.0 ** -9},
 }
+ALLOWANCE_FRACTION = 1e-3
 
 
 def gpu_inputs(w: wl.Workload, rank: int, k_glob=None, v_glob=None, device="cuda"):
@@ -89,15 +93,25 @@ def compare(w: wl.Workload, out_rows: np.ndarray, lse_rows: np.ndarray, want_o: 
         bound = np.maximum(tol["max_abs"], tol["rel_ulp"] * np.abs(want_o))
         stats["worst_excess"] = float((err / bound).max())
         stats["mean_bound"] = tol["mean_abs"] + tol["mean_rel"] * float(np.abs(want_o).mean())
+        stats["allowance_used"] = int((err > tol["max_abs"]).sum())
+        stats["elements"] = int(err.size)
     return stats
 
 
-def check(w: wl.Workload, stats: dict) -> None:
+def check(w: wl.Workload, stats: dict, allowance: bool = True) -> None:
+    """Assert the bounds above.  allowance=False: the stated bf16 bounds with
+    no output-format allowance (the named workloads)."""
     tol = TOL[w.dtype]
     msg = f"{w.name}: {stats} vs {tol}"
-    if "rel_ulp" in tol:
+    if "rel_ulp" in tol and allowance:
+        print(f"[gpu]   {w.name}: {stats['allowance_used']} of {stats['elements']} elements use the "
+              f"output-format allowance", flush=True)
         assert stats["worst_excess"] <= 1.0, msg
         assert stats["mean_abs"] <= stats["mean_bound"], msg
+        assert stats["allowance_used"] <= ALLOWANCE_FRACTION * stats["elements"], msg
+    elif "rel_ulp" in tol:
+        assert stats["max_abs"] <= tol["max_abs"], msg
+        assert stats["mean_abs"] <= tol["mean_abs"], msg
     else:
         assert stats["max_abs"] <= tol["max_abs"], msg
     assert stats["lse_max_abs"] <= tol["lse_max_abs"], msg
