@@ -175,6 +175,31 @@ int ringattn_decode_partial(const void* q, const void* k, const void* v, int n_q
                             int64_t n_keys, int Hq, int Hkv, int d_h,
                             float* m, float* z, float* y, void* stream);
 
+/*
+ * ringattn_decode_partial_noalloc -- ringattn_decode_partial for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, same kernels and
+ * bit-identical results, but the chunk partials live in a static device
+ * buffer of the library instead of a stream-ordered allocation.  The call
+ * makes no hipMalloc, hipFree or other allocating call.
+ *
+ *  Limit: the call needs 2 * round_up(4 * ceil(n_keys / 256) * Hq * n_q, 256)
+ *  + 4 * ceil(n_keys / 256) * Hq * n_q * d_h bytes of scratch, at most 32 MiB
+ *  (e.g. 31,250 keys x 64/8 heads x d 128 takes 4.1 MB; one 131,072-key shard
+ *  x 4/1 heads 1.1 MB).  A larger call returns RINGATTN_EUNSUPPORTED before
+ *  any HIP call.
+ *  The buffer: one per device, 32 MiB, held by every device the library runs
+ *  on until the process ends.  Every call on a device uses the same buffer:
+ *  calls that overlap on one device (other streams, other threads) race and
+ *  give wrong results; calls on one stream, or ordered by events, are safe.
+ *  Nothing in it needs to start at zero: each call writes every partial it
+ *  reads.  The first call on a device looks up the buffer's device address.
+ *  These calls are not timed by ringattn_timing_enable.
+ */
+int ringattn_decode_partial_noalloc(const void* q, const void* k, const void* v, int n_q,
+                                    int64_t n_keys, int Hq, int Hkv, int d_h,
+                                    float* m, float* z, float* y, void* stream);
+
 /* Static string for a status code. */
 const char* ringattn_status_string(int status);
 

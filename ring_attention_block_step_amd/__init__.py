@@ -20,7 +20,7 @@ import os
 
 import torch
 
-__all__ = ["forward", "backward", "merge", "decode_partial", "shard_index", "pack_shards", "lib", "RingAttnError",
+__all__ = ["forward", "backward", "merge", "decode_partial", "decode_partial_noalloc", "shard_index", "pack_shards", "lib", "RingAttnError",
            "timing_enable", "timing_collect", "timing_collect_decode", "timing_collect_backward", "set_serial_hops",
            "redo_count", "version", "SYMBOLS", "LIB_PATH"]
 
@@ -29,7 +29,7 @@ LAYOUTS = {"contiguous": 0, "striped": 1, "zigzag": 2}
 
 # Every symbol include/ringattn.h declares.
 SYMBOLS = ("ringattn_forward", "ringattn_forward_f32", "ringattn_backward", "ringattn_merge",
-           "ringattn_decode_partial", "ringattn_status_string", "ringattn_last_error", "ringattn_timing_enable",
+           "ringattn_decode_partial", "ringattn_decode_partial_noalloc", "ringattn_status_string", "ringattn_last_error", "ringattn_timing_enable",
            "ringattn_timing_collect", "ringattn_timing_collect_backward", "ringattn_timing_collect_decode",
            "ringattn_redo_count", "ringattn_set_serial_hops", "ringattn_version")
 
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.ringattn_timing_collect_backward.restype = i32
     L.ringattn_decode_partial.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp]
     L.ringattn_decode_partial.restype = i32
+    L.ringattn_decode_partial_noalloc.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp]
+    L.ringattn_decode_partial_noalloc.restype = i32
     L.ringattn_status_string.argtypes = [i32]
     L.ringattn_status_string.restype = ctypes.c_char_p
     L.ringattn_last_error.argtypes = []
@@ -255,13 +257,14 @@ def merge(m: torch.Tensor, z: torch.Tensor, y: torch.Tensor, *, out_dtype=torch.
 
 
 def decode_partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, m: torch.Tensor | None = None,
-                   z: torch.Tensor | None = None, y: torch.Tensor | None = None):
+                   z: torch.Tensor | None = None, y: torch.Tensor | None = None, no_alloc: bool = False):
     """Partial (m, z, y) of new query rows q [n_q, Hq, d] against a resident
     shard k, v [n_keys, Hkv, d], all bf16 on one device (n_keys may be 0).
 
     Returns m, z [Hq, n_q] (natural log) and y [n_q, Hq, d], fp32; pass views
     of part p of merge's inputs ([P, Hq, n_q], [P, n_q, Hq, d]) to fill them
-    in place.  Asynchronous on the current stream of q's device.
+    in place.  Asynchronous on the current stream of q's device.  no_alloc:
+    call ringattn_decode_partial_noalloc (the library's static scratch).
     """
     L = lib()
     _need(q.is_cuda and k.is_cuda and v.is_cuda and q.device == k.device == v.device,
@@ -282,9 +285,19 @@ def decode_partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, m: torc
         _need(tuple(t.shape) == shape and t.dtype == torch.float32 and t.is_contiguous() and t.device == q.device,
               f"{name} must be float32 {list(shape)} on q's device")
     with torch.cuda.device(q.device):
-        _check(L.ringattn_decode_partial(_ptr(q), _ptr(k) if n_keys else None, _ptr(v) if n_keys else None,
-                                         n_q, n_keys, Hq, Hkv, d, _ptr(m), _ptr(z), _ptr(y), _stream(q.device)))
+        fn = L.ringattn_decode_partial_noalloc if no_alloc else L.ringattn_decode_partial
+        _check(fn(_ptr(q), _ptr(k) if n_keys else None, _ptr(v) if n_keys else None,
+                  n_q, n_keys, Hq, Hkv, d, _ptr(m), _ptr(z), _ptr(y), _stream(q.device)))
     return m, z, y
+
+
+def decode_partial_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, m: torch.Tensor | None = None,
+                           z: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """decode_partial through ringattn_decode_partial_noalloc: the library
+    allocates nothing (its chunk partials use a static 32 MiB device buffer;
+    calls that overlap on one device race).  Outputs made here when not given
+    are the caller's allocations."""
+    return decode_partial(q, k, v, m=m, z=z, y=y, no_alloc=True)
 
 
 def timing_enable(flag: bool = True) -> None:

@@ -18,10 +18,22 @@
 // its value rows global -> LDS with direct loads (1 KB of whole rows per wave
 // instruction, each 16 bytes landing in a swizzled chunk of its row), where
 // the p*V product reads them transposed without bank conflicts.
+#include <mutex>
+
 #include "internal.h"
 
 namespace ringattn {
 namespace {
+
+// Scratch of the allocation-free entry point: the chunk partials (m, z, y) of
+// one call, kDecodeScratchBytes at most.  One copy per device, held for the
+// life of the process.  Host code never passes this name to a kernel: it
+// passes the device address that hipGetSymbolAddress returns for the current
+// device (decode_scratch()).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -359,6 +371,22 @@ void launch_all(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t st) {
   if (D == 128)

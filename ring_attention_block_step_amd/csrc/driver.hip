@@ -274,6 +274,54 @@ int collect_timing(int kinds, double* sums, int64_t* counts) {
   return status;
 }
 
+// Checks the arguments of a decode partial and fills everything but the
+// workspace pointers; the workspace takes ws_bytes: m and z partials of
+// mz_bytes each, then the y partials.
+int decode_args(const void* q, const void* k, const void* v, int n_q, int64_t n_keys, int Hq, int Hkv, int d_h,
+                float* m, float* z, float* y, DecodeArgs* a, size_t* mz_bytes, size_t* ws_bytes) {
+  if (!q || !m || !z || !y) return fail(RINGATTN_EINVAL, "q, m, z and y must be non-null");
+  if (n_keys > 0 && (!k || !v)) return fail(RINGATTN_EINVAL, "k and v must be non-null when n_keys > 0");
+  if (!aligned16(q) || (n_keys > 0 && (!aligned16(k) || !aligned16(v))))
+    return fail(RINGATTN_EINVAL, "q, k and v must be 16-byte aligned");
+  if (!aligned16(y) || ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(z)) & 3))
+    return fail(RINGATTN_EINVAL, "y must be 16-byte aligned, m and z 4-byte aligned");
+  if (n_q < 1) return fail(RINGATTN_EINVAL, "n_q must be >= 1 (got %d)", n_q);
+  if (n_keys < 0) return fail(RINGATTN_EINVAL, "n_keys must be >= 0");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(RINGATTN_EINVAL, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (got %d, %d)", Hq, Hkv);
+  if (d_h != 64 && d_h != 128) return fail(RINGATTN_EUNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
+  const int64_t rows = (int64_t)(Hq / Hkv) * n_q;
+  const int64_t nchunks = (n_keys + kDecodeChunk - 1) / kDecodeChunk;
+  if (rows * Hkv > ((int64_t)1 << 30) || nchunks > ((int64_t)1 << 30) || (rows + 15) / 16 > 65535)
+    return fail(RINGATTN_EUNSUPPORTED, "decode shape too large (n_q=%d, Hq=%d, n_keys=%lld)", n_q, Hq,
+                (long long)n_keys);
+  a->q = static_cast<const __bf16*>(q);
+  a->k = static_cast<const __bf16*>(k);
+  a->v = static_cast<const __bf16*>(v);
+  a->m_out = m;
+  a->z_out = z;
+  a->y_out = y;
+  a->n_keys = n_keys;
+  a->n_q = n_q;
+  a->Hq = Hq;
+  a->Hkv = Hkv;
+  a->G = Hq / Hkv;
+  a->rows = (int)rows;
+  a->nchunks = (int)nchunks;
+  a->sl2 = (float)(1.4426950408889634 / std::sqrt((double)d_h));
+  a->ws_m = a->ws_z = a->ws_y = nullptr;
+  const size_t parts = (size_t)nchunks * Hkv * rows;
+  *mz_bytes = round_up(parts * sizeof(float), 256);
+  *ws_bytes = 2 * *mz_bytes + parts * d_h * sizeof(float);
+  return RINGATTN_OK;
+}
+
+void set_decode_workspace(DecodeArgs* a, void* ws, size_t mz_bytes) {
+  a->ws_m = static_cast<float*>(ws);
+  a->ws_z = reinterpret_cast<float*>(static_cast<char*>(ws) + mz_bytes);
+  a->ws_y = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * mz_bytes);
+}
+
 }  // namespace
 
 extern "C" {
@@ -472,52 +520,36 @@ int ringattn_merge(const float* m, const float* z, const float* y, int nparts, i
 
 int ringattn_decode_partial(const void* q, const void* k, const void* v, int n_q, int64_t n_keys, int Hq, int Hkv,
                             int d_h, float* m, float* z, float* y, void* stream) {
-  if (!q || !m || !z || !y) return fail(RINGATTN_EINVAL, "q, m, z and y must be non-null");
-  if (n_keys > 0 && (!k || !v)) return fail(RINGATTN_EINVAL, "k and v must be non-null when n_keys > 0");
-  if (!aligned16(q) || (n_keys > 0 && (!aligned16(k) || !aligned16(v))))
-    return fail(RINGATTN_EINVAL, "q, k and v must be 16-byte aligned");
-  if (!aligned16(y) || ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(z)) & 3))
-    return fail(RINGATTN_EINVAL, "y must be 16-byte aligned, m and z 4-byte aligned");
-  if (n_q < 1) return fail(RINGATTN_EINVAL, "n_q must be >= 1 (got %d)", n_q);
-  if (n_keys < 0) return fail(RINGATTN_EINVAL, "n_keys must be >= 0");
-  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
-    return fail(RINGATTN_EINVAL, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (got %d, %d)", Hq, Hkv);
-  if (d_h != 64 && d_h != 128) return fail(RINGATTN_EUNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
-  const int64_t rows = (int64_t)(Hq / Hkv) * n_q;
-  const int64_t nchunks = (n_keys + kDecodeChunk - 1) / kDecodeChunk;
-  if (rows * Hkv > ((int64_t)1 << 30) || nchunks > ((int64_t)1 << 30) || (rows + 15) / 16 > 65535)
-    return fail(RINGATTN_EUNSUPPORTED, "decode shape too large (n_q=%d, Hq=%d, n_keys=%lld)", n_q, Hq,
-                (long long)n_keys);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   DecodeArgs a;
-  a.q = static_cast<const __bf16*>(q);
-  a.k = static_cast<const __bf16*>(k);
-  a.v = static_cast<const __bf16*>(v);
-  a.m_out = m;
-  a.z_out = z;
-  a.y_out = y;
-  a.n_keys = n_keys;
-  a.n_q = n_q;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.G = Hq / Hkv;
-  a.rows = (int)rows;
-  a.nchunks = (int)nchunks;
-  a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)d_h));
-  const size_t parts = (size_t)nchunks * Hkv * rows;
-  const size_t mz_bytes = round_up(parts * sizeof(float), 256);
-  const size_t ws_bytes = 2 * mz_bytes + parts * d_h * sizeof(float);
+  size_t mz_bytes = 0, ws_bytes = 0;
+  int rc = decode_args(q, k, v, n_q, n_keys, Hq, Hkv, d_h, m, z, y, &a, &mz_bytes, &ws_bytes);
+  if (rc != RINGATTN_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
   void* ws = nullptr;
   if (ws_bytes > 0) HIP_TRY(hipMallocAsync(&ws, ws_bytes, st));
-  a.ws_m = static_cast<float*>(ws);
-  a.ws_z = reinterpret_cast<float*>(static_cast<char*>(ws) + mz_bytes);
-  a.ws_y = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * mz_bytes);
+  set_decode_workspace(&a, ws, mz_bytes);
   const int tix = timing_begin(st, 2);
   hipError_t e = launch_decode(a, d_h, st);
   timing_end(tix, st);
   hipError_t fe = ws ? hipFreeAsync(ws, st) : hipSuccess;
   if (e != hipSuccess) return fail(RINGATTN_EHIP, "decode launch failed: %s", hipGetErrorString(e));
   if (fe != hipSuccess) return fail(RINGATTN_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+  return RINGATTN_OK;
+}
+
+int ringattn_decode_partial_noalloc(const void* q, const void* k, const void* v, int n_q, int64_t n_keys, int Hq,
+                                    int Hkv, int d_h, float* m, float* z, float* y, void* stream) {
+  DecodeArgs a;
+  size_t mz_bytes = 0, ws_bytes = 0;
+  int rc = decode_args(q, k, v, n_q, n_keys, Hq, Hkv, d_h, m, z, y, &a, &mz_bytes, &ws_bytes);
+  if (rc != RINGATTN_OK) return rc;
+  if (ws_bytes > kDecodeScratchBytes)
+    return fail(RINGATTN_EUNSUPPORTED, "decode needs %zu bytes of scratch, more than the %zu of the static buffer",
+                ws_bytes, kDecodeScratchBytes);
+  void* ws = nullptr;
+  HIP_TRY(decode_scratch(&ws));
+  set_decode_workspace(&a, ws, mz_bytes);
+  HIP_TRY(launch_decode(a, d_h, static_cast<hipStream_t>(stream)));
   return RINGATTN_OK;
 }
 

@@ -158,6 +158,12 @@ hipError_t launch_merge(const float* m, const float* z, const float* y, int npar
                         int Hq, int D, void* out, int out_f32, float* lse, hipStream_t st);
 // Chunk kernel (skipped when nchunks == 0), then the combine kernel.
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t st);
+// The allocation-free decode's scratch: a static device array of
+// kDecodeScratchBytes, one per device.  decode_scratch() returns its device
+// address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t{32} << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t decode_scratch(void** ptr);
 
 
 }  // namespace ringattn

@@ -123,6 +123,20 @@ def test_decode_rejects_bad_arguments():
     assert "too large" in L.ringattn_last_error().decode()
 
 
+def test_decode_noalloc_rejects_bad_arguments_and_calls_beyond_its_scratch():
+    """The allocation-free decode checks its arguments like the decode entry
+    point and refuses a call whose chunk partials exceed its 32 MiB static
+    buffer, before any HIP call: ceil(1e6 / 256) chunks x 8 key/value heads x
+    8 rows x (128 + 2) floats is about 130 MB."""
+    L = _lib()
+    d = L.ringattn_decode_partial_noalloc
+    assert d(None, FAKE, FAKE, 1, 10, 4, 1, 128, FAKE, FAKE, FAKE, None) == 1
+    assert d(FAKE, FAKE, FAKE, 1, 10, 6, 4, 128, FAKE, FAKE, FAKE, None) == 1
+    assert d(FAKE, FAKE, FAKE, 1, 10, 4, 1, 96, FAKE, FAKE, FAKE, None) == 2
+    assert d(FAKE, FAKE, FAKE, 1, 10 ** 6, 64, 8, 128, FAKE, FAKE, FAKE, None) == 2
+    assert "scratch" in L.ringattn_last_error().decode()
+
+
 def test_backward_rejects_bad_arguments():
     L = _lib()
     f32 = ctypes.POINTER(ctypes.c_float)
