@@ -159,44 +159,65 @@ def _blas_threads() -> int:
 
 
 def cpu_baseline(w, rank, k_glob, v_glob, seconds: float, gpu_out=None, gpu_lse=None):
-    """Time oracle.dense_attention on growing batches of sampled query rows until
-    about ``seconds`` of work; report useful fp64 TFLOP/s over exactly those rows."""
+    """Time oracle.dense_attention on growing batches of the 4096 sampled query
+    rows (per head) that the parity checks use, until about ``seconds`` of
+    work; report useful fp64 TFLOP/s over exactly the rows timed, with BLAS
+    on every host core this process may run on.  The times for all 4096
+    sampled rows and for the whole share are extrapolated from the timed rows
+    by their allowed pairs, and labelled so."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
     import workloads as wl
 
+    host_cores = len(os.sched_getaffinity(0))
     k = k_glob.double().numpy()
     v = v_glob.double().numpy()
     tq_all = oracle.shard_positions(w.layout, rank, w.P, w.b)
     rows = wl.sample_local_rows(w.b, min(w.b, 4096), w.seed, 0)
-    done, elapsed, flops = 0, 0.0, 0.0
+
+    def allowed(tq):
+        return (tq + 1) if w.causal else np.full(tq.shape, w.N)
+
+    done, elapsed, pairs_done = 0, 0.0, 0
     batch = 4
     max_err = mean_err_sum = 0.0
     n_err = 0
-    while done < rows.size and elapsed < seconds:
-        sel = rows[done:done + batch]
-        tq = tq_all[sel]
-        q = wl.query_rows(w, tq).double().numpy()
-        t0 = time.perf_counter()
-        o, lse = oracle.dense_attention(q, tq, k, v, w.causal)
-        elapsed += time.perf_counter() - t0
-        allowed = (tq + 1) if w.causal else np.full(tq.shape, w.N)
-        flops += 4.0 * w.d * float(allowed.sum()) * w.Hq
-        if gpu_out is not None:
-            err = np.abs(gpu_out[sel].astype(np.float64) - o)
-            max_err = max(max_err, float(err.max()))
-            mean_err_sum += float(err.sum())
-            n_err += err.size
-        done += sel.size
-        batch = min(batch * 2, 256)
+    with threadpool_limits(host_cores, user_api="blas"):
+        blas = _blas_threads()
+        while done < rows.size and elapsed < seconds:
+            sel = rows[done:done + batch]
+            tq = tq_all[sel]
+            q = wl.query_rows(w, tq).double().numpy()
+            t0 = time.perf_counter()
+            o, lse = oracle.dense_attention(q, tq, k, v, w.causal)
+            elapsed += time.perf_counter() - t0
+            pairs_done += int(allowed(tq).sum())
+            if gpu_out is not None:
+                err = np.abs(gpu_out[sel].astype(np.float64) - o)
+                max_err = max(max_err, float(err.max()))
+                mean_err_sum += float(err.sum())
+                n_err += err.size
+            done += sel.size
+            batch = min(batch * 2, 256)
+    flops = 4.0 * w.d * pairs_done * w.Hq
+    pairs_sample = int(allowed(tq_all[rows]).sum())
+    pairs_full = int(allowed(tq_all).sum())
+    per_pair = elapsed / max(1, pairs_done)
     res = {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
-        "cores": _blas_threads(),
+        "cores": host_cores,
+        "blas_threads": blas,
         "kind": "oracle",
-        "sample": (f"{done} sampled query rows x {w.Hq} heads of rank {rank} "
+        "sample": (f"{done} of the 4096 sampled query rows x {w.Hq} heads of rank {rank} "
                    f"({w.name}); fp64 NumPy dense oracle; {elapsed:.1f} s"),
+        "rows_timed_per_head": int(done),
+        "seconds_timed": elapsed,
+        "extrapolated_4096_rows_per_head_s": per_pair * pairs_sample,
+        "extrapolated_full_share_s": per_pair * pairs_full,
+        "extrapolation": "seconds per allowed pair of the timed rows x allowed pairs (extrapolated, not timed)",
     }
     parity = None
     if gpu_out is not None and n_err:
