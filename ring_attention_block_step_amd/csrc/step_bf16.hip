@@ -15,10 +15,11 @@
 //
 // Workgroup: 8/NT waves = 8/NT query items (query head, 32*NT rows) that share
 // one key/value head, so every key/value tile staged in LDS serves 256 queries
-// (NT = 2: one wave per SIMD; NT = 1: two waves per SIMD).  Tiles of 64 keys move global -> LDS with direct-to-LDS loads
-// (global_load_lds_dwordx4); the slot layout already is the LDS image, stored
-// chunk-major so the fragment reads are conflict-free and need no per-lane
-// address arithmetic.
+// (NT = 2: one wave per SIMD; NT = 1: two waves per SIMD).  Tiles of 64 keys
+// move global -> LDS with direct-to-LDS buffer loads (buffer_load_dwordx4 ...
+// lds, scalar addresses only); the slot layout already is the LDS image,
+// stored chunk-major so the fragment reads are conflict-free and need no
+// per-lane address arithmetic.
 //
 // Software pipeline over the tiles every row of the workgroup sees in full,
 // in half tiles of 32 keys: block h issues the MFMAs of PV(h-1) and S(h+1)
@@ -53,6 +54,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Fourth word of a raw buffer resource on gfx9-family chips: untyped 32-bit
+// data, no swizzle, bounds checked against the record count.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_t* p) { return (uint32_t)(uintptr_t)p; }
 
@@ -107,12 +113,17 @@ struct Step {
 
   // Direct global -> LDS copy of one tile; each wave moves PER_WAVE chunks of
   // 1 KB (64 lanes x 16 bytes), landing verbatim at the same offset in LDS.
-  static __device__ __forceinline__ void load_tile(const unsigned char* g, lds_t* l, int wave, int lane) {
+  // The copy goes through a buffer resource based at the tile: the lane's
+  // offset (lane16 = 16 lane) is fixed and the wave's first chunk (wchunk,
+  // bytes) is wave-uniform, so the loop spends no vector instructions on
+  // addresses.  The resource spans exactly one tile.
+  static __device__ __forceinline__ void load_tile(const unsigned char* g, lds_t* l, uint32_t lane16,
+                                                   uint32_t wchunk) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, TILE, kBufferRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int c = wave * PER_WAVE + i;
-      __builtin_amdgcn_global_load_lds(g + c * 1024 + lane * 16, l + c * 1024, 16, 0, 0);
-    }
+    for (int i = 0; i < PER_WAVE; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(l + wchunk + i * 1024), 16, lane16, wchunk + i * 1024,
+                                               0, 0);
   }
 
   // S^T of one half tile (32 keys, rows half*32 ..) x 32*NT queries: s[nt].
@@ -508,8 +519,10 @@ void step_bf16_kernel(StepBf16Args a) {
   // Tile t lands in buffer kbuf(t) / vbuf(t).  The source index is clamped to
   // the last tile, so a prefetch past the end reads valid memory into a buffer
   // that no later iteration reads.
-  auto issue_k = [&](int t) { S::load_tile(kg + (size_t)min(t, T - 1) * S::TILE, kbuf(t), wave, lane); };
-  auto issue_v = [&](int t) { S::load_tile(vg + (size_t)min(t, T - 1) * S::TILE, vbuf(t), wave, lane); };
+  const uint32_t lane16 = (uint32_t)(lane * 16);
+  const uint32_t wchunk = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (S::PER_WAVE * 1024);
+  auto issue_k = [&](int t) { S::load_tile(kg + (size_t)min(t, T - 1) * S::TILE, kbuf(t), lane16, wchunk); };
+  auto issue_v = [&](int t) { S::load_tile(vg + (size_t)min(t, T - 1) * S::TILE, vbuf(t), lane16, wchunk); };
 
   // Every iteration t issues V(t+2) and K(t+3), and at its end waits for
   // everything but those (the loads of iteration t-1: V(t+1), K(t+2)) before
