@@ -70,8 +70,8 @@ enum { RINGATTN_LAYOUT_CONTIGUOUS = 0, RINGATTN_LAYOUT_STRIPED = 1, RINGATTN_LAY
  *  d_h                      64 or 128
  *  causal                   0 or 1
  *  layout                   RINGATTN_LAYOUT_CONTIGUOUS, _STRIPED or _ZIGZAG
- *  Limits: b <= 2^28 and Hq * b <= 2^25 (the kernels index rows in 32 bits);
- *  a larger shard returns RINGATTN_EUNSUPPORTED.
+ *  Limits: b <= 2^28, Hq * b <= 2^25 and Hkv <= 65536 (the kernels index
+ *  rows in 32 bits); a larger shape returns RINGATTN_EUNSUPPORTED.
  *
  * The library allocates its workspace (two key/value slots and the fp32 running
  * state) stream-ordered on `stream` and frees it the same way.  The block for

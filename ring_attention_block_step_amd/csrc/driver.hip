@@ -178,6 +178,7 @@ int check_forward_args(const void* q, const void* k, const void* v, const void* 
   const int64_t b = N / P;
   if (b > (int64_t)1 << 28 || (int64_t)Hq * b > ((int64_t)1 << 31) / 64)
     return fail(RINGATTN_EUNSUPPORTED, "shard too large (b=%lld, Hq=%d)", (long long)b, Hq);
+  if (Hkv > 65536) return fail(RINGATTN_EUNSUPPORTED, "too many key/value heads (Hkv=%d > 65536)", Hkv);
   return RINGATTN_OK;
 }
 

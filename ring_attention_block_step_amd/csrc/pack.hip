@@ -21,42 +21,64 @@
 namespace ringattn {
 namespace {
 
+// One workgroup of 256 threads per (64-key tile, key/value head, half of d):
+// it copies its half of the key tile's 16-byte chunks and transposes its half
+// of the value tile's d-rows through LDS.  Splitting d keeps the LDS at
+// 64 x (D/2 + 8) bf16 (9 KB for d = 128); tile bases are scalars and each
+// thread moves one 16-byte chunk at a time, which keeps the registers at 16.
+// That is what a step workgroup leaves free on its compute unit, so the hop
+// can run beside the step it overlaps.  Rows b .. bpad-1 of the last tile are
+// zero.  The launcher requires Hkv * D * 64 < 2^31 (32-bit row offsets).
 template <int D>
 __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                         uint16_t* __restrict__ kp, uint16_t* __restrict__ vp,
                                                         int b, int bpad, int Hkv) {
   constexpr int T = kKeyTile;
-  constexpr int CPR = D / 8;                 // 16-byte chunks per row of D bf16
-  constexpr int CHUNKS = T * CPR;            // chunks per tile
-  constexpr int VS = D + 8;                  // LDS row pitch (elements) of the value tile
+  constexpr int DH = D / 2;                  // d of this workgroup's half
+  constexpr int CPR = DH / 8;                // 16-byte chunks per row of the half
+  constexpr int ITER = T * CPR / 256;        // chunks per thread
+  constexpr int VS = DH + 8;                 // LDS row pitch (elements) of the value half-tile
+  static_assert(ITER >= 1 && T * CPR % 256 == 0, "a tile half must split over 256 threads");
   __shared__ uint16_t vs[T * VS];
 
   const int t = blockIdx.x;
   const int h = blockIdx.y;
+  const int half = blockIdx.z;
   const int ntiles = bpad / T;
+  const int rows = min(T, b - t * T);        // rows of this tile inside the shard
+  const uint32_t rstride = (uint32_t)Hkv * D; // elements from one row to the next
+  const size_t base = ((size_t)t * T * Hkv + h) * D + half * DH;
+  const uint16_t* ks = k + base;
+  const uint16_t* vsrc = v + base;
+  unsigned char* kt = reinterpret_cast<unsigned char*>(kp + ((size_t)h * ntiles + t) * (size_t)(D * T));
+  unsigned char* vt = reinterpret_cast<unsigned char*>(vp + ((size_t)h * ntiles + t) * (size_t)(D * T));
 
-  for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
-    const int row = c / CPR;
-    const int cc = c % CPR;
-    const int j = t * T + row;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (j < b) {
-      const size_t src = ((size_t)j * Hkv + h) * D + cc * 8;
-      kv = *reinterpret_cast<const uint4*>(k + src);
-      vv = *reinterpret_cast<const uint4*>(v + src);
-    }
-    unsigned char* kt = reinterpret_cast<unsigned char*>(kp + ((size_t)h * ntiles + t) * (size_t)(D * T));
-    *reinterpret_cast<uint4*>(kt + key_tile_off(row, cc)) = kv;
+#pragma unroll 1
+  for (int i = 0; i < ITER; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
+    const int row = c / CPR, cc = c % CPR;
+    uint4 vv = make_uint4(0, 0, 0, 0);
+    if (row < rows) vv = *reinterpret_cast<const uint4*>(vsrc + row * rstride + cc * 8);
     uint16_t* dst = vs + row * VS + cc * 8;
     *reinterpret_cast<uint2*>(dst) = make_uint2(vv.x, vv.y);
     *reinterpret_cast<uint2*>(dst + 4) = make_uint2(vv.z, vv.w);
   }
+#pragma unroll 1
+  for (int i = 0; i < ITER; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
+    const int row = c / CPR, cc = c % CPR;
+    uint4 kv = make_uint4(0, 0, 0, 0);
+    if (row < rows) kv = *reinterpret_cast<const uint4*>(ks + row * rstride + cc * 8);
+    *reinterpret_cast<uint4*>(kt + key_tile_off(row, half * CPR + cc)) = kv;
+  }
   __syncthreads();
 
-  // Output chunk c: d-row c / 8, storage positions (c % 8) * 8 .. +7.
-  unsigned char* vt = reinterpret_cast<unsigned char*>(vp + ((size_t)h * ntiles + t) * (size_t)(D * T));
-  for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
-    const int d = c / (T / 8);
+  // Output chunk c of the half: d-row half * DH + c / 8, storage positions
+  // (c % 8) * 8 .. +7.
+#pragma unroll 1
+  for (int i = 0; i < ITER; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
+    const int dl = c / (T / 8);
     const int k0 = (c % (T / 8)) * 8;
     uint32_t w[4];
 #pragma unroll
@@ -68,11 +90,11 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* __restri
         const int g = kappa & ~15;
         const int in = kappa & 15;
         const int key = g + ((in & 3) | ((in & 4) << 1) | ((in & 8) >> 1));
-        pair[x] = vs[key * VS + d];
+        pair[x] = vs[key * VS + dl];
       }
       w[e / 2] = pair[0] | (pair[1] << 16);
     }
-    *reinterpret_cast<uint4*>(vt + val_tile_off<D>(d, k0 / 8)) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(vt + val_tile_off<D>(half * DH + dl, k0 / 8)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -80,7 +102,8 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* __restri
 
 hipError_t launch_pack_bf16(const __bf16* k_shard, const __bf16* v_shard, __bf16* kp, __bf16* vp,
                             int b, int bpad, int Hkv, int D, hipStream_t st) {
-  dim3 grid(bpad / kKeyTile, Hkv);
+  if ((int64_t)Hkv * D * kKeyTile >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  dim3 grid(bpad / kKeyTile, Hkv, 2);
   const uint16_t* k = reinterpret_cast<const uint16_t*>(k_shard);
   const uint16_t* v = reinterpret_cast<const uint16_t*>(v_shard);
   uint16_t* kd = reinterpret_cast<uint16_t*>(kp);

@@ -79,6 +79,7 @@ def _fwd(fn, **kw):
     (dict(d=256), 2, "d_h"),
     (dict(N=1 << 31, P=4, Hq=4, Hkv=2), 2, "too large"),
     (dict(N=4 << 20, P=4, Hq=64, Hkv=8), 2, "too large"),
+    (dict(N=1024, P=4, Hq=1 << 17, Hkv=1 << 17), 2, "key/value heads"),
 ])
 def test_forward_rejects_bad_arguments(entry, kw, status, needle):
     L = _lib()
