@@ -17,7 +17,9 @@ host cores on a bounded sample of query rows of the same workload.
 striped and zigzag layouts, 32k and 128k shares), and
 ``backward_other_workloads`` the backward on the 128k share.
 ``reference_gemm`` times the vendor's dense bf16 GEMM on the same GPU (the
-practical dense-MFMA rate under sustained load, for context).
+practical dense-MFMA rate under sustained load, for context), and
+``reference_attention`` the vendor's own fused causal attention forward (torch
+SDPA, flash backend) on a 16k-token, 32-head input, both for context.
 ``sclk_during_timed_region`` is the engine clock the driver reported while the
 timed steps ran, and ``pct_of_bf16_peak_at_measured_clock`` the rate against
 the peak scaled to that clock.
@@ -346,6 +348,41 @@ def measure_reference_gemm(n: int = 16384, reps: int = 10) -> dict:
             "value": tflops, "unit": "TFLOP/s", "frac_of_peak": tflops / PEAK_BF16_TFLOPS}
 
 
+def measure_reference_attention(heads: int = 32, seq: int = 16384, d: int = 128, reps: int = 5) -> dict | None:
+    """Context, not a step of the path: the vendor's own fused attention
+    forward (torch's scaled_dot_product_attention restricted to its flash
+    backend, bf16, causal, batch 1) on the same GPU in the same run, as useful
+    (mask-aware) TFLOP/s: 4 d FLOPs per allowed pair and head.  Restricting the
+    backend means a missing flash kernel raises here instead of running the
+    bf16 math path; then the field is None."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    g = torch.Generator(device="cuda").manual_seed(13)
+    q, k, v = (torch.randn(1, heads, seq, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    try:
+        with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+            for _ in range(2):
+                o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+            e1.record()
+            torch.cuda.synchronize()
+    except RuntimeError as e:
+        print(f"[bench] reference attention unavailable: {e}", file=sys.stderr, flush=True)
+        return None
+    ms = e0.elapsed_time(e1) / reps
+    flops = useful_flops(seq * (seq + 1) // 2, d, heads)
+    del q, k, v, o
+    return {"op": "torch scaled_dot_product_attention, flash backend, bf16, causal", "shape":
+            {"batch": 1, "heads": heads, "seq": seq, "d_h": d}, "ms": ms, "value": flops / (ms * 1e-3) / 1e12,
+            "unit": "TFLOP/s", "frac_of_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def measure_decode(name: str = "decode-31k-gqa64", reps: int = 20) -> dict:
     """Time ringattn_decode_partial on one resident shard of a decode workload
     (HIP events around the call's kernels, inside the library) and report the
@@ -522,7 +559,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true", help="skip the merge-kernel measurement")
-    ap.add_argument("--no-gemm-ref", action="store_true", help="skip the vendor bf16 GEMM reference measurement")
+    ap.add_argument("--no-gemm-ref", action="store_true",
+                    help="skip the vendor bf16 GEMM and attention reference measurements")
     ap.add_argument("--no-workloads", action="store_true", help="skip the forward on the other named workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-kernel measurement")
     ap.add_argument("--decode-workload", default="decode-31k-gqa64",
@@ -632,6 +670,7 @@ def main(argv=None) -> int:
 
     merge = None if args.no_merge else measure_merge()
     gemm = None if args.no_gemm_ref else measure_reference_gemm()
+    attn_ref = None if args.no_gemm_ref else measure_reference_attention()
     others = None if args.no_workloads else measure_workloads()
     decode = None if args.no_decode else measure_decode(args.decode_workload)
     backward = None if args.no_backward else measure_backward(args.backward_workload, reps=10)
@@ -669,6 +708,8 @@ def main(argv=None) -> int:
         "other_workloads": others,
         "reference_gemm": gemm,
         "step_kernel_vs_reference_gemm": (achieved / gemm["value"]) if (gemm and achieved) else None,
+        "reference_attention": attn_ref,
+        "value_vs_reference_attention": (value / attn_ref["value"]) if attn_ref else None,
         "merge_kernel": merge,
         "decode_kernel": decode,
         "backward": backward,
