@@ -240,8 +240,19 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const lds_t* l) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_t*>(l))));
 }
-__device__ __forceinline__ void load_lds16(const unsigned char* g, lds_t* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+// Fourth word of a raw buffer resource on gfx9-family chips: untyped 32-bit
+// data, no swizzle, bounds checked against the record count.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// Direct global -> LDS copy of `n` consecutive 1 KB chunks of a block through
+// a buffer resource based at the block: chunk c moves 16 bytes per lane from
+// byte 1024 c + lane16 to LDS l + 1024 c.  The lane offset is fixed and the
+// chunk offset wave-uniform, so the copy spends no vector instructions on
+// addresses.  `bytes` bounds the resource.
+__device__ __forceinline__ void copy_chunks(const unsigned char* g, uint32_t bytes, lds_t* l, uint32_t lane16,
+                                            uint32_t chunk) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, bytes, kBufferRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(l + chunk * 1024), 16, lane16,
+                                           chunk * 1024, 0, 0);
 }
 __device__ __forceinline__ uint32_t lds_addr(const lds_t* p) { return (uint32_t)(uintptr_t)p; }
 
@@ -321,6 +332,7 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
+  const uint32_t lane16 = (uint32_t)(lane * 16);
   const bool scorer = wave < kDkvPairs;
   const int pair = scorer ? wave : wave - kDkvPairs;
   // XCD-aware placement: workgroup L runs on XCD L % kXcds, and consecutive
@@ -373,8 +385,8 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
     lds_t* l = buf(it);
 #pragma unroll
     for (int i = 0; i < PWX; ++i) {
-      const int c = wave + kDkvPairs * i;
-      if (i < PW || c < IT::CHUNKS) load_lds16(g + c * 1024 + lane * 16, l + c * 1024);
+      const int c = __builtin_amdgcn_readfirstlane(wave) + kDkvPairs * i;
+      if (i < PW || c < IT::CHUNKS) copy_chunks(g, IT::BYTES, l, lane16, (uint32_t)c);
     }
   };
   // Wait until this wave's copies of all but the newest AHEAD items landed
@@ -618,6 +630,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
+  const uint32_t lane16 = (uint32_t)(lane * 16);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int kvh = blockIdx.x % a.Hkv;
   const int wgi = a.dq_wgs_per_head - 1 - (int)(blockIdx.x / a.Hkv);
   const int item = wgi * kDqWaves + wave;
@@ -671,8 +685,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
     const unsigned char* g = kg + (size_t)min(t, T - 1) * KB::BYTES + comp;
 #pragma unroll
     for (int i = 0; i < PWC; ++i) {
-      const int c = wave * PWC + i;
-      load_lds16(g + c * 1024 + lane * 16, dst + c * 1024);
+      const int c = wave_u * PWC + i;
+      copy_chunks(g, KB::TILE, dst, lane16, (uint32_t)c);
     }
   };
   auto begin_iter = [&](int t) {
