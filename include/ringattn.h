@@ -42,6 +42,9 @@ enum {
 
 enum { RINGATTN_LAYOUT_CONTIGUOUS = 0, RINGATTN_LAYOUT_STRIPED = 1, RINGATTN_LAYOUT_ZIGZAG = 2 };
 
+/* How the next visit's key/value block reaches its slot (ringattn_set_hop_mode). */
+enum { RINGATTN_HOP_FUSED = 0, RINGATTN_HOP_SERIAL = 1, RINGATTN_HOP_STREAMS = 2 };
+
 /*
  * ringattn_forward -- rank `rank`'s share of the ring, bf16 in and out.
  *
@@ -244,9 +247,27 @@ int ringattn_timing_collect_decode(double* decode_ms, int64_t* decode_calls);
 int ringattn_redo_count(int64_t* redone, int64_t* redone_late_fold);
 
 /*
- * Debug switch: when serial = 1 every key/value hop copy runs on the caller's
- * stream instead of the library's second stream (no overlap).  Results are
- * bit-identical either way; used to test the double buffer for races.
+ * How the ring's hop (the next visit's key/value block copied into the free
+ * slot of the double buffer; "Ring Attention" (darshanfofadiya.com), 4.5
+ * "Communication-Computation Overlap") is scheduled, for every later call on
+ * any device:
+ *   RINGATTN_HOP_FUSED   (default) the step launch of visit i also copies the
+ *                        block of visit i+1, in its workgroups' tails, so the
+ *                        copy overlaps the step inside one launch and no
+ *                        cross-stream event is needed.  Entry points whose
+ *                        step kernel has no copy (ringattn_forward_f32,
+ *                        ringattn_backward) use RINGATTN_HOP_STREAMS instead;
+ *   RINGATTN_HOP_SERIAL  a copy kernel on the caller's stream between steps;
+ *   RINGATTN_HOP_STREAMS a copy kernel on the library's second stream beside
+ *                        the next step, ordered by events.
+ * Results are bit-identical in every mode.  Returns RINGATTN_EINVAL for
+ * another value.
+ */
+int ringattn_set_hop_mode(int mode);
+
+/*
+ * Earlier form of ringattn_set_hop_mode: serial = 1 selects
+ * RINGATTN_HOP_SERIAL, 0 RINGATTN_HOP_FUSED.
  */
 int ringattn_set_serial_hops(int serial);
 

@@ -21,7 +21,7 @@ import os
 import torch
 
 __all__ = ["forward", "backward", "merge", "decode_partial", "decode_partial_noalloc", "shard_index", "pack_shards", "lib", "RingAttnError",
-           "timing_enable", "timing_collect", "timing_collect_decode", "timing_collect_backward", "set_serial_hops",
+           "timing_enable", "timing_collect", "timing_collect_decode", "timing_collect_backward", "set_serial_hops", "set_hop_mode", "HOP_MODES",
            "redo_count", "version", "SYMBOLS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
@@ -31,7 +31,7 @@ LAYOUTS = {"contiguous": 0, "striped": 1, "zigzag": 2}
 SYMBOLS = ("ringattn_forward", "ringattn_forward_f32", "ringattn_backward", "ringattn_merge",
            "ringattn_decode_partial", "ringattn_decode_partial_noalloc", "ringattn_status_string", "ringattn_last_error", "ringattn_timing_enable",
            "ringattn_timing_collect", "ringattn_timing_collect_backward", "ringattn_timing_collect_decode",
-           "ringattn_redo_count", "ringattn_set_serial_hops", "ringattn_version")
+           "ringattn_redo_count", "ringattn_set_hop_mode", "ringattn_set_serial_hops", "ringattn_version")
 
 _lib = None
 
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.ringattn_redo_count.restype = i32
     L.ringattn_set_serial_hops.argtypes = [i32]
     L.ringattn_set_serial_hops.restype = i32
+    L.ringattn_set_hop_mode.argtypes = [i32]
+    L.ringattn_set_hop_mode.restype = i32
     L.ringattn_version.argtypes = []
     L.ringattn_version.restype = ctypes.c_char_p
     _lib = L
@@ -335,7 +337,20 @@ def redo_count() -> dict:
     return {"redone": a.value, "redone_late_fold": b.value}
 
 
+HOP_MODES = {"fused": 0, "serial": 1, "streams": 2}
+
+
+def set_hop_mode(mode: str) -> None:
+    """Schedule of the ring's hop copies for later calls: "fused" (the step
+    launch of visit i copies the block of visit i+1; the default), "serial"
+    (copy kernels on the caller's stream) or "streams" (copy kernels on the
+    library's second stream, ordered by events)."""
+    _check(lib().ringattn_set_hop_mode(HOP_MODES[mode]))
+
+
 def set_serial_hops(flag: bool) -> None:
+    """True: hop copies serialised on the caller's stream; False: the default
+    fused schedule."""
     _check(lib().ringattn_set_serial_hops(int(bool(flag))))
 
 

@@ -71,7 +71,8 @@ std::mutex g_timing_mu;
 bool g_timing = false;
 std::vector<TimedLaunch> g_timed;
 
-bool g_serial_hops = false;
+// How the next visit's block reaches its slot (ringattn_set_hop_mode).
+int g_hop_mode = RINGATTN_HOP_FUSED;
 
 int device_ctx(DeviceCtx** out) {
   int dev = 0;
@@ -186,10 +187,13 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: two key/value slots, then `extra_bytes` for the step kernels'
 // state (init() prepares it once per call).  step(slot, extra, i, r, mask,
-// carry_in, last, stream) runs visit i, of block r.
+// carry_in, last, stream, next_r, next_slot) runs visit i, of block r; with
+// next_r >= 0 its launch also copies block next_r into next_slot (fused hops,
+// only where the caller passes fusable = true).  hop_into(r, slot, stream)
+// copies block r into a slot with a kernel of its own.
 template <typename StepFn, typename HopFn, typename InitFn>
 int run_ring(int P, int rank, int b, int causal, int layout, size_t slot_bytes, size_t extra_bytes, hipStream_t st,
-             HopFn hop_into, StepFn step, InitFn init, int timing_kind = 0) {
+             HopFn hop_into, StepFn step, InitFn init, bool fusable, int timing_kind = 0) {
   DeviceCtx* ctx = nullptr;
   int rc = device_ctx(&ctx);
   if (rc != RINGATTN_OK) return rc;
@@ -204,8 +208,9 @@ int run_ring(int P, int rank, int b, int causal, int layout, size_t slot_bytes, 
   const int n = (int)visits.size();  // >= 1: the own block is never fully masked
 
   std::lock_guard<std::mutex> lk(ctx->mu);
-  const bool serial = g_serial_hops;
-  hipStream_t hs = serial ? st : ctx->hop;
+  const int mode = (g_hop_mode == RINGATTN_HOP_FUSED && !fusable) ? RINGATTN_HOP_STREAMS : g_hop_mode;
+  const bool streams = mode == RINGATTN_HOP_STREAMS;
+  hipStream_t hs = streams ? ctx->hop : st;
 
   void* ws = nullptr;
   HIP_TRY(hipMallocAsync(&ws, 2 * slot_bytes + extra_bytes, st));
@@ -213,8 +218,25 @@ int run_ring(int P, int rank, int b, int causal, int layout, size_t slot_bytes, 
   char* extra = static_cast<char*>(ws) + 2 * slot_bytes;
 
   int status = RINGATTN_OK;
-  auto run = [&]() -> int {
-    if (!serial) {
+  // Fused: one stream; the launch of visit i copies the block of visit i+1
+  // into the slot that visit i-1 read, which that launch's predecessor on the
+  // stream has finished with.
+  auto run_fused = [&]() -> int {
+    HIP_TRY(init(extra, st));
+    HIP_TRY(hop_into(visits[0].r, slot[0], st));
+    for (int i = 0; i < n; ++i) {
+      const int next_r = i + 1 < n ? visits[i + 1].r : -1;
+      const int tix = timing_begin(st, timing_kind);
+      HIP_TRY(step(slot[i & 1], extra, i, visits[i].r, visits[i].mask, i > 0, i == n - 1, st, next_r,
+                   slot[(i + 1) & 1]));
+      timing_end(tix, st);
+    }
+    return RINGATTN_OK;
+  };
+  // Separate hop kernels, on the library's copy stream (ordered by events)
+  // or serialised on the caller's stream.
+  auto run_kernels = [&]() -> int {
+    if (streams) {
       HIP_TRY(hipEventRecord(ctx->ev_start, st));
       HIP_TRY(hipStreamWaitEvent(hs, ctx->ev_start, 0));
     }
@@ -222,25 +244,25 @@ int run_ring(int P, int rank, int b, int causal, int layout, size_t slot_bytes, 
     HIP_TRY(hop_into(visits[0].r, slot[0], st));
     if (n > 1) {
       HIP_TRY(hop_into(visits[1].r, slot[1], hs));
-      if (!serial) HIP_TRY(hipEventRecord(ctx->ev_ready[1], hs));
+      if (streams) HIP_TRY(hipEventRecord(ctx->ev_ready[1], hs));
     }
     for (int i = 0; i < n; ++i) {
-      if (i > 0 && !serial) HIP_TRY(hipStreamWaitEvent(st, ctx->ev_ready[i & 1], 0));
+      if (i > 0 && streams) HIP_TRY(hipStreamWaitEvent(st, ctx->ev_ready[i & 1], 0));
       const int tix = timing_begin(st, timing_kind);
-      HIP_TRY(step(slot[i & 1], extra, i, visits[i].r, visits[i].mask, i > 0, i == n - 1, st));
+      HIP_TRY(step(slot[i & 1], extra, i, visits[i].r, visits[i].mask, i > 0, i == n - 1, st, -1, nullptr));
       timing_end(tix, st);
       if (i + 2 < n) {
-        if (!serial) {
+        if (streams) {
           HIP_TRY(hipEventRecord(ctx->ev_done[i & 1], st));
           HIP_TRY(hipStreamWaitEvent(hs, ctx->ev_done[i & 1], 0));
         }
         HIP_TRY(hop_into(visits[i + 2].r, slot[i & 1], hs));
-        if (!serial) HIP_TRY(hipEventRecord(ctx->ev_ready[i & 1], hs));
+        if (streams) HIP_TRY(hipEventRecord(ctx->ev_ready[i & 1], hs));
       }
     }
     return RINGATTN_OK;
   };
-  status = run();
+  status = mode == RINGATTN_HOP_FUSED ? run_fused() : run_kernels();
   // Every copy-stream operation was waited on by the caller stream before its
   // slot was read, so freeing on the caller stream is ordered after all of them.
   hipError_t fe = hipFreeAsync(ws, st);
@@ -369,8 +391,15 @@ int ringattn_forward(const void* q, const void* k, const void* v, void* out, flo
   };
   auto init = [&](char*, hipStream_t) -> hipError_t { return hipSuccess; };
   auto step = [&](char* slot, char* extra, int i, int, const BlockMask& mk, bool carry_in, bool last,
-                  hipStream_t s) -> hipError_t {
+                  hipStream_t s, int next_r, char* next_slot) -> hipError_t {
     StepBf16Args x = a;
+    x.hop = HopBf16{nullptr, nullptr, nullptr, nullptr};
+    if (next_r >= 0) {
+      x.hop.k = reinterpret_cast<const uint16_t*>(kb + (size_t)next_r * shard_elems);
+      x.hop.v = reinterpret_cast<const uint16_t*>(vb + (size_t)next_r * shard_elems);
+      x.hop.kp = reinterpret_cast<uint16_t*>(next_slot);
+      x.hop.vp = x.hop.kp + kv_elems;
+    }
     char* cin = extra + (size_t)((i + 1) & 1) * carry_bytes;   // written by step i-1
     char* cout = extra + (size_t)(i & 1) * carry_bytes;
     x.kp = reinterpret_cast<const __bf16*>(slot);
@@ -388,7 +417,7 @@ int ringattn_forward(const void* q, const void* k, const void* v, void* out, flo
     x.last = last;
     return launch_step_bf16(x, D, s);
   };
-  return run_ring(P, rank, b, causal, layout, slot_bytes, extra_bytes, st, hop, step, init);
+  return run_ring(P, rank, b, causal, layout, slot_bytes, extra_bytes, st, hop, step, init, true);
 }
 
 int ringattn_forward_f32(const float* q, const float* k, const float* v, float* out, float* lse, int64_t N, int P,
@@ -413,7 +442,7 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
   };
   auto init = [](char*, hipStream_t) -> hipError_t { return hipSuccess; };
   auto step = [&](char* slot, char* carry, int, int, const BlockMask& mk, bool carry_in, bool last,
-                  hipStream_t s) -> hipError_t {
+                  hipStream_t s, int, char*) -> hipError_t {
     StepF32Args a;
     a.q = q;
     a.k = reinterpret_cast<const float*>(slot);
@@ -435,7 +464,7 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
     a.scale = (float)(1.0 / std::sqrt((double)D));
     return launch_step_f32(a, D, s);
   };
-  return run_ring(P, rank, b, causal, layout, slot_bytes, carry_bytes, st, hop, step, init);
+  return run_ring(P, rank, b, causal, layout, slot_bytes, carry_bytes, st, hop, step, init, false);
 }
 
 int ringattn_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -483,7 +512,7 @@ int ringattn_backward(const void* q, const void* k, const void* v, const void* o
     return launch_bwd_prep(x, D, s);
   };
   auto step = [&](char* slot, char* extra, int, int r, const BlockMask& mk, bool carry_in, bool,
-                  hipStream_t s) -> hipError_t {
+                  hipStream_t s, int, char*) -> hipError_t {
     BwdArgs x = a;
     x.items = extra;
     x.kslot = slot;
@@ -497,7 +526,7 @@ int ringattn_backward(const void* q, const void* k, const void* v, const void* o
     x.dq_accumulate = carry_in;
     return launch_bwd_step(x, D, s);
   };
-  return run_ring(P, rank, b, causal, layout, slot_bytes, items_bytes, st, hop, step, init, 3);
+  return run_ring(P, rank, b, causal, layout, slot_bytes, items_bytes, st, hop, step, init, false, 3);
 }
 
 int ringattn_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows, int Hq, int d_h,
@@ -609,8 +638,15 @@ int ringattn_redo_count(int64_t* redone, int64_t* redone_late_fold) {
   return RINGATTN_OK;
 }
 
+int ringattn_set_hop_mode(int mode) {
+  if (mode != RINGATTN_HOP_FUSED && mode != RINGATTN_HOP_SERIAL && mode != RINGATTN_HOP_STREAMS)
+    return fail(RINGATTN_EINVAL, "hop mode must be 0 (fused), 1 (serial) or 2 (streams), got %d", mode);
+  g_hop_mode = mode;
+  return RINGATTN_OK;
+}
+
 int ringattn_set_serial_hops(int serial) {
-  g_serial_hops = serial != 0;
+  g_hop_mode = serial != 0 ? RINGATTN_HOP_SERIAL : RINGATTN_HOP_FUSED;
   return RINGATTN_OK;
 }
 

@@ -35,6 +35,15 @@ struct BlockMask {
   int qbeg;   // rows i < qbeg see no key of this block
 };
 
+// Hop copy that a step launch carries: the next visit's shard [b, Hkv, D]
+// into the free slot, in the layout pack_bf16_kernel writes.  k == null: none.
+struct HopBf16 {
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* kp;      // slot key tiles
+  uint16_t* vp;      // slot value tiles
+};
+
 struct StepBf16Args {
   const __bf16* q;   // [b, Hq, D] caller's query rows
   const __bf16* kp;  // slot keys   [Hkv][bpad/64] tiles of 64 x D, chunk-major (key_tile_off)
@@ -56,6 +65,7 @@ struct StepBf16Args {
   int carry_in;      // read the running state instead of starting empty
   int last;          // finish: write O and LSE instead of the running state
   float sl2;         // log2(e) / sqrt(D)
+  HopBf16 hop;       // copied by the workgroups after their tiles
 };
 
 struct StepF32Args {

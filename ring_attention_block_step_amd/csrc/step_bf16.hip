@@ -44,6 +44,7 @@
 #include <utility>
 
 #include "internal.h"
+#include "pack_unit.h"
 
 namespace ringattn {
 namespace {
@@ -696,46 +697,95 @@ void step_bf16_kernel(StepBf16Args a) {
     wait_all_and_sync();
   }
 
-  if (!active) return;
-
-  if (a.last) {
+  // The next visit's hop copy: (64-key tile, key/value head) units spread over
+  // the workgroups, both halves of d at once (threads 0-255 and 256-511), in
+  // the LDS the tiles no longer use.  The first unit's loads are issued before
+  // the outputs below, so their latency passes while those stores issue.
+  // Every wave takes part: each unit has a barrier after its LDS writes and
+  // one after its LDS reads.
+  using PH = PackHalf<D>;
+  static_assert(2 * PH::LDS_ELEMS * 2 <= (int)sizeof(smem_raw), "hop copy fits the tile LDS");
+  const bool hop = a.hop.k != nullptr;
+  const int hop_units = hop ? (a.bpad / kKeyTile) * a.Hkv : 0;
+  uint16_t* hop_lds = reinterpret_cast<uint16_t*>(smem_raw) + (tid >> 8) * PH::LDS_ELEMS;
+  auto hop_unit = [&](int u) {
+    return PH(a.hop.k, a.hop.v, a.hop.kp, a.hop.vp, a.b, a.bpad, a.Hkv, u / a.Hkv, u % a.Hkv, tid >> 8, tid & 255,
+              hop_lds);
+  };
+  uint4 hv[PH::ITER], hk[PH::ITER];
+  int u = (int)blockIdx.x;
+  if (u < hop_units) {
+    const PH p = hop_unit(u);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float zt = zs[nt] + __shfl_xor(zs[nt], 32);
-      const int qi = q0 + nt * 32 + l32;
-      if (qi < a.b) {
-        const float inv = zt > 0.f ? 1.0f / zt : 0.f;
-        __bf16* orow = a.out + ((size_t)qi * a.Hq + hq) * D;
+    for (int i = 0; i < PH::ITER; ++i) {
+      hv[i] = p.load_v(i);
+      hk[i] = p.load_k(i);
+    }
+  }
+
+  // Outputs of the workgroup's rows: O and LSE after the last visit, else the
+  // running state.
+  if (active) {
+    if (a.last) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float zt = zs[nt] + __shfl_xor(zs[nt], 32);
+        const int qi = q0 + nt * 32 + l32;
+        if (qi < a.b) {
+          const float inv = zt > 0.f ? 1.0f / zt : 0.f;
+          __bf16* orow = a.out + ((size_t)qi * a.Hq + hq) * D;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const f32x2 lo = {o[nt][dt][rg * 4 + 0] * inv, o[nt][dt][rg * 4 + 1] * inv};
+              const f32x2 hv = {o[nt][dt][rg * 4 + 2] * inv, o[nt][dt][rg * 4 + 3] * inv};
+              uint2 w;
+              w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+              w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hv, bf16x2));
+              *reinterpret_cast<uint2*>(orow + dt * 32 + rg * 8 + hi * 4) = w;
+            }
+          if (a.lse && hi == 0)
+            a.lse[(size_t)hq * a.b + qi] = zt > 0.f ? (mref[nt] + __log2f(zt)) * kLn2 : -INFINITY;
+        }
+      }
+    } else {
+      float* cy = a.cyo + ig * ystride;
+      float* cm = a.cmo + ig * (NT * 64);
+      float* cz = a.czo + ig * (NT * 64);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        cm[nt * 64 + lane] = mref[nt];
+        cz[nt * 64 + lane] = zs[nt];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const f32x2 lo = {o[nt][dt][rg * 4 + 0] * inv, o[nt][dt][rg * 4 + 1] * inv};
-            const f32x2 hv = {o[nt][dt][rg * 4 + 2] * inv, o[nt][dt][rg * 4 + 3] * inv};
-            uint2 w;
-            w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-            w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hv, bf16x2));
-            *reinterpret_cast<uint2*>(orow + dt * 32 + rg * 8 + hi * 4) = w;
-          }
-        if (a.lse && hi == 0)
-          a.lse[(size_t)hq * a.b + qi] = zt > 0.f ? (mref[nt] + __log2f(zt)) * kLn2 : -INFINITY;
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<float4*>(cy + carry_off<DT>(nt, dt, r4, lane)) =
+                make_float4(o[nt][dt][4 * r4], o[nt][dt][4 * r4 + 1], o[nt][dt][4 * r4 + 2], o[nt][dt][4 * r4 + 3]);
       }
     }
-  } else {
-    float* cy = a.cyo + ig * ystride;
-    float* cm = a.cmo + ig * (NT * 64);
-    float* cz = a.czo + ig * (NT * 64);
+  }
+
+
+  for (; u < hop_units; u += (int)gridDim.x) {
+    const PH p = hop_unit(u);
+    if (u != (int)blockIdx.x) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      cm[nt * 64 + lane] = mref[nt];
-      cz[nt * 64 + lane] = zs[nt];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<float4*>(cy + carry_off<DT>(nt, dt, r4, lane)) =
-              make_float4(o[nt][dt][4 * r4], o[nt][dt][4 * r4 + 1], o[nt][dt][4 * r4 + 2], o[nt][dt][4 * r4 + 3]);
+      for (int i = 0; i < PH::ITER; ++i) {
+        hv[i] = p.load_v(i);
+        hk[i] = p.load_k(i);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < PH::ITER; ++i) {
+      p.v_to_lds(i, hv[i]);
+      p.store_k(i, hk[i]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PH::ITER; ++i) p.store_vt(i);
+    __syncthreads();
   }
 }
 
@@ -754,6 +804,7 @@ hipError_t take_step_bf16_redo_counts(unsigned long long counts[2]) {
 }
 
 hipError_t launch_step_bf16(const StepBf16Args& a, int D, hipStream_t st) {
+  if (a.hop.k != nullptr && (int64_t)a.Hkv * D * kKeyTile >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)step_bf16_grid(a));
   const dim3 block(64 * kStepWaves);
   if (D == 128)

@@ -176,6 +176,16 @@ def test_timing_collect_empty():
     assert ra.timing_collect() == {"step_ms": 0.0, "step_launches": 0, "merge_ms": 0.0, "merge_launches": 0}
 
 
+def test_hop_mode_accepts_the_three_schedules_and_rejects_others():
+    L = _lib()
+    for mode in (3, -1, 100):
+        assert L.ringattn_set_hop_mode(mode) == 1
+        assert "hop mode" in L.ringattn_last_error().decode()
+    for name in ("serial", "streams", "fused"):
+        ra.set_hop_mode(name)
+    assert L.ringattn_set_serial_hops(1) == 0 and L.ringattn_set_serial_hops(0) == 0
+
+
 def test_binding_raises_on_error_status():
     L = _lib()
     rc = _fwd(L.ringattn_forward, P=0)

@@ -128,19 +128,20 @@ def test_backward_medium_all_rows():
     _check("dv", gv.cpu().double().numpy(), wv, "medium rank 5")
 
 
-def test_backward_serial_and_overlapped_hops_are_bit_identical():
+def test_backward_hop_modes_are_bit_identical():
     N, P, Hq, Hkv, d = 1024, 4, 4, 2, 128
     q, k, v, do = _inputs(N, P, Hq, Hkv, d, seed=7)
     res = []
-    for serial in (False, True):
-        ra.set_serial_hops(serial)
+    for mode in ("fused", "serial", "streams"):
+        ra.set_hop_mode(mode)
         try:
             (gq, gk, gv), _ = _run_rank(q, k, v, do, N, P, 3, "contiguous", True, Hq, Hkv, d)
         finally:
-            ra.set_serial_hops(False)
+            ra.set_hop_mode("fused")
         res.append((gq.cpu(), gk.cpu(), gv.cpu()))
-    for a, b_ in zip(*res):
-        assert torch.equal(a, b_)
+    for other in res[1:]:
+        for a, b_ in zip(res[0], other):
+            assert torch.equal(a, b_)
 
 
 @pytest.mark.parametrize("name", ["32k-contiguous-causal", "128k-contiguous-causal"])

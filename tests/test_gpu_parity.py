@@ -250,20 +250,27 @@ def test_late_dominant_key_after_late_fold(layout, d):
     assert total["redone_late_fold"] > 0, total
 
 
-def test_serial_and_overlapped_hops_are_bit_identical():
-    """The double buffer on the second stream must not race: outputs with the hop
-    copies serialised on the caller stream are bit-identical."""
-    w = _w("race", N=8192, P=8, ranks=(7,), Hq=8, Hkv=2)
-    q, k, v = gpu_inputs(w, 7)
+@pytest.mark.parametrize("N,P,Hq,Hkv,d,layout", [
+    (8192, 8, 8, 2, 128, "contiguous"),   # one hop unit per step workgroup
+    (8192, 8, 4, 4, 128, "striped"),      # G = 1: four units per workgroup
+    (4000, 4, 16, 2, 64, "contiguous"),   # G = 8, ragged shard (b = 1000): zero rows in the last tile
+    (6144, 4, 6, 3, 128, "zigzag"),       # odd head count
+])
+def test_hop_modes_are_bit_identical(N, P, Hq, Hkv, d, layout):
+    """The double buffer must not race in any hop schedule: the copies fused
+    into the step launches, serialised on the caller stream, or on the second
+    stream give bit-identical outputs."""
+    w = _w("race", N=N, P=P, ranks=(P - 1,), Hq=Hq, Hkv=Hkv, d=d, layout=layout)
+    q, k, v = gpu_inputs(w, P - 1)
     outs = []
     try:
-        for serial in (False, True, False):
-            ra.set_serial_hops(serial)
-            out, lse = ra.forward(q, k, v, P=w.P, rank=7, causal=True, layout="contiguous")
+        for mode in ("fused", "serial", "streams", "fused"):
+            ra.set_hop_mode(mode)
+            out, lse = ra.forward(q, k, v, P=w.P, rank=P - 1, causal=True, layout=layout)
             torch.cuda.synchronize()
             outs.append((out.clone(), lse.clone()))
     finally:
-        ra.set_serial_hops(False)
+        ra.set_hop_mode("fused")
     for o, l in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
 
