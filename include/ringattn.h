@@ -254,9 +254,11 @@ int ringattn_redo_count(int64_t* redone, int64_t* redone_late_fold);
  *   RINGATTN_HOP_FUSED   (default) the step launch of visit i also copies the
  *                        block of visit i+1, in its workgroups' tails, so the
  *                        copy overlaps the step inside one launch and no
- *                        cross-stream event is needed.  Entry points whose
- *                        step kernel has no copy (ringattn_forward_f32,
- *                        ringattn_backward) use RINGATTN_HOP_STREAMS instead;
+ *                        cross-stream event is needed (ringattn_backward:
+ *                        the dK/dV launch of visit i copies the block of
+ *                        visit i+1 before its own work).  ringattn_forward_f32,
+ *                        whose step kernel has no copy, uses
+ *                        RINGATTN_HOP_STREAMS instead;
  *   RINGATTN_HOP_SERIAL  a copy kernel on the caller's stream between steps;
  *   RINGATTN_HOP_STREAMS a copy kernel on the library's second stream beside
  *                        the next step, ordered by events.

@@ -161,32 +161,47 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 
 // Slot of the dQ kernel: per key/value head, tiles of 64 keys holding K and V
 // row-major and K^T transposed (keys in storage order); rows b .. bpad-1 zero.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                       unsigned char* __restrict__ slot, int b, int bpad, int Hkv) {
+// Tile t of head h by NTH threads (tid < NTH) with (T x (D + 8)) uint16 of LDS
+// at ks: every thread first loads all of its chunks, then stores them, then
+// (after one workgroup barrier, which every thread of the workgroup must reach
+// the same number of times) writes its chunks of K^T.
+template <int D, int NTH>
+__device__ __forceinline__ void bwd_pack_tile(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                              unsigned char* __restrict__ slot, int b, int bpad, int Hkv, int t, int h,
+                                              int tid, uint16_t* ks) {
   constexpr int T = kKeyTile;
   constexpr int CPR = D / 8;
   constexpr int VS = D + 8;
-  __shared__ uint16_t ks[T * VS];
-  const int t = blockIdx.x, h = blockIdx.y;
+  constexpr int ITER = T * CPR / NTH;
+  static_assert(ITER >= 1 && T * CPR % NTH == 0, "a tile splits evenly over the threads");
   const int ntiles = bpad / T;
   unsigned char* blk = slot + ((size_t)h * ntiles + t) * KBlock<D>::BYTES;
-  for (int c = threadIdx.x; c < T * CPR; c += 256) {
+  uint4 kv[ITER], vv[ITER];
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int c = tid + NTH * i;
     const int row = c / CPR, cc = c % CPR;
     const int j = t * T + row;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    kv[i] = vv[i] = make_uint4(0, 0, 0, 0);
     if (j < b) {
       const size_t src = ((size_t)j * Hkv + h) * D + cc * 8;
-      kv = *reinterpret_cast<const uint4*>(k + src);
-      vv = *reinterpret_cast<const uint4*>(v + src);
+      kv[i] = *reinterpret_cast<const uint4*>(k + src);
+      vv[i] = *reinterpret_cast<const uint4*>(v + src);
     }
-    *reinterpret_cast<uint4*>(blk + KBlock<D>::K + key_tile_off(row, cc)) = kv;
-    *reinterpret_cast<uint4*>(blk + KBlock<D>::V + key_tile_off(row, cc)) = vv;
-    *reinterpret_cast<uint2*>(ks + row * VS + cc * 8) = make_uint2(kv.x, kv.y);
-    *reinterpret_cast<uint2*>(ks + row * VS + cc * 8 + 4) = make_uint2(kv.z, kv.w);
+  }
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int c = tid + NTH * i;
+    const int row = c / CPR, cc = c % CPR;
+    *reinterpret_cast<uint4*>(blk + KBlock<D>::K + key_tile_off(row, cc)) = kv[i];
+    *reinterpret_cast<uint4*>(blk + KBlock<D>::V + key_tile_off(row, cc)) = vv[i];
+    *reinterpret_cast<uint2*>(ks + row * VS + cc * 8) = make_uint2(kv[i].x, kv[i].y);
+    *reinterpret_cast<uint2*>(ks + row * VS + cc * 8 + 4) = make_uint2(kv[i].z, kv[i].w);
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < T * CPR; c += 256) {
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int c = tid + NTH * i;
     const int d = c / (T / 8);
     const int k0 = (c % (T / 8)) * 8;
     uint32_t w[4];
@@ -202,6 +217,13 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t* __restric
     }
     *reinterpret_cast<uint4*>(blk + KBlock<D>::KT + val_tile_off<D>(d, k0 / 8)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                       unsigned char* __restrict__ slot, int b, int bpad, int Hkv) {
+  __shared__ uint16_t ks[kKeyTile * (D + 8)];
+  bwd_pack_tile<D, 256>(k, v, slot, b, bpad, Hkv, (int)blockIdx.x, (int)blockIdx.y, (int)threadIdx.x, ks);
 }
 
 // An empty volatile statement that takes an MFMA result: the MFMA may no
@@ -333,6 +355,23 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const uint32_t lane16 = (uint32_t)(lane * 16);
+
+  // The next visit's hop copy, before this launch's own work: (64-key tile,
+  // key/value head) units of the dQ kernel's slot spread over the
+  // workgroups, in LDS that the item ring overwrites only after the barrier
+  // that follows each unit.
+  static_assert(kKeyTile * (D + 8) * 2 <= (int)sizeof(smem_raw), "hop copy fits the item ring");
+  if (a.hop_k != nullptr) {
+    const int units = (a.bpad / kKeyTile) * a.Hkv;
+    for (int u = (int)blockIdx.x; u < units; u += (int)gridDim.x) {
+      bwd_pack_tile<D, 64 * kDkvWaves>(reinterpret_cast<const uint16_t*>(a.hop_k),
+                                       reinterpret_cast<const uint16_t*>(a.hop_v),
+                                       static_cast<unsigned char*>(a.hop_slot), a.b, a.bpad, a.Hkv, u / a.Hkv,
+                                       u % a.Hkv, tid, reinterpret_cast<uint16_t*>(smem_raw));
+      __syncthreads();
+    }
+  }
+
   const bool scorer = wave < kDkvPairs;
   const int pair = scorer ? wave : wave - kDkvPairs;
   // XCD-aware placement: workgroup L runs on XCD L % kXcds, and consecutive

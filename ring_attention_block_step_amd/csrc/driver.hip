@@ -512,10 +512,13 @@ int ringattn_backward(const void* q, const void* k, const void* v, const void* o
     return launch_bwd_prep(x, D, s);
   };
   auto step = [&](char* slot, char* extra, int, int r, const BlockMask& mk, bool carry_in, bool,
-                  hipStream_t s, int, char*) -> hipError_t {
+                  hipStream_t s, int next_r, char* next_slot) -> hipError_t {
     BwdArgs x = a;
     x.items = extra;
     x.kslot = slot;
+    x.hop_k = next_r >= 0 ? kb + (size_t)next_r * shard_elems : nullptr;
+    x.hop_v = next_r >= 0 ? vb + (size_t)next_r * shard_elems : nullptr;
+    x.hop_slot = next_r >= 0 ? next_slot : nullptr;
     x.k = kb + (size_t)r * shard_elems;
     x.v = vb + (size_t)r * shard_elems;
     x.dk = dk + (size_t)r * shard_elems;
@@ -526,7 +529,7 @@ int ringattn_backward(const void* q, const void* k, const void* v, const void* o
     x.dq_accumulate = carry_in;
     return launch_bwd_step(x, D, s);
   };
-  return run_ring(P, rank, b, causal, layout, slot_bytes, items_bytes, st, hop, step, init, false, 3);
+  return run_ring(P, rank, b, causal, layout, slot_bytes, items_bytes, st, hop, step, init, true, 3);
 }
 
 int ringattn_merge(const float* m, const float* z, const float* y, int nparts, int64_t rows, int Hq, int d_h,

@@ -103,6 +103,11 @@ struct BwdArgs {
   int dq_accumulate;              // add into dq (later visits) instead of writing it
   float sl2;                      // log2(e) / sqrt(D)
   float scale;                    // 1 / sqrt(D)
+  // Hop copy the dK/dV launch carries: the next visit's shard into the free
+  // dQ-kernel slot (the layout bwd_pack_kernel writes).  hop_k == null: none.
+  const __bf16* hop_k;
+  const __bf16* hop_v;
+  void* hop_slot;
 };
 size_t bwd_item_bytes(int D);
 size_t bwd_kblock_bytes(int D);
