@@ -1,9 +1,9 @@
 """Throughput of one device's share of a causal Ring Attention forward pass.
 
 One "step" is one call of the whole hot path for rank u: the P ring steps (hop
-copies into the double buffer, the step kernels with the online-softmax fold,
-the fused O/LSE epilogue) over one batch of synthetic input already resident in
-HBM.  Default workload: the million-token share (N = 1,048,576, P = 8, contiguous
+copies into the double buffer, by default carried in the tails of the step
+launches; the step kernels with the online-softmax fold; the fused O/LSE
+epilogue) over one batch of synthetic input already resident in HBM.  Default workload: the million-token share (N = 1,048,576, P = 8, contiguous
 shards, rank 7, 4 query heads / 1 key-value head, d_h = 128, bf16, K scaled by 2,
 causal).
 
@@ -34,6 +34,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-decode] [--decode-workload NAME] [--decode-only]
                        [--no-backward] [--backward-workload NAME] [--backward-only]
                        [--no-gemm-ref] [--no-workloads] [--merge-only]
+                       [--hop-mode fused|serial|streams]
 """
 
 from __future__ import annotations
@@ -53,7 +54,9 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_bf16_traffic.json")
 MERGE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "merge_traffic.json")
 MERGE_SOURCE = os.path.join(ROOT, "ring_attention_block_step_amd", "csrc", "merge.hip")
-STEP_SOURCE = os.path.join(ROOT, "ring_attention_block_step_amd", "csrc", "step_bf16.hip")
+# Sources of the step kernel (its own file and the hop copy it carries).
+STEP_SOURCE = (os.path.join(ROOT, "ring_attention_block_step_amd", "csrc", "step_bf16.hip"),
+               os.path.join(ROOT, "ring_attention_block_step_amd", "csrc", "pack_unit.h"))
 
 
 # ---------------------------------------------------------------------------
@@ -115,9 +118,13 @@ def hop_bytes(b: int, d: int, heads_kv: int, elem_bytes: int) -> int:
     return 2 * b * d * heads_kv * elem_bytes
 
 
-def source_digest(path: str = STEP_SOURCE) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(path=STEP_SOURCE) -> str:
+    """sha256 (16 hex digits) of a source file, or of several concatenated."""
+    h = hashlib.sha256()
+    for p in ([path] if isinstance(path, str) else path):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -574,6 +581,8 @@ def main(argv=None) -> int:
                     help="only run the backward measurement and print its JSON object")
     ap.add_argument("--merge-only", action="store_true",
                     help="only run the merge-kernel measurement and print its JSON object")
+    ap.add_argument("--hop-mode", default="fused", choices=("fused", "serial", "streams"),
+                    help="schedule of the ring's hop copies (ringattn_set_hop_mode)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -592,6 +601,7 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         return 3
+    ra.set_hop_mode(args.hop_mode)
     if args.decode_only:
         print(json.dumps(measure_decode(args.decode_workload)), flush=True)
         return 0
@@ -697,7 +707,8 @@ def main(argv=None) -> int:
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded; Q,K,V as the workload states)",
         "config": {"workload": w.name, "N": w.N, "P": w.P, "b": w.b, "rank": rank, "layout": w.layout,
-                   "causal": w.causal, "Hq": w.Hq, "Hkv": w.Hkv, "d_h": w.d, "useful_flops": flops},
+                   "causal": w.causal, "Hq": w.Hq, "Hkv": w.Hkv, "d_h": w.d, "useful_flops": flops,
+                   "hop_mode": args.hop_mode},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "sclk_during_timed_region": sclk,
         "pct_of_bf16_peak_at_measured_clock": (100.0 * value / (PEAK_BF16_TFLOPS * sclk["mean_mhz"] /
