@@ -34,7 +34,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-decode] [--decode-workload NAME] [--decode-only]
                        [--no-backward] [--backward-workload NAME] [--backward-only]
                        [--no-gemm-ref] [--no-workloads] [--merge-only]
-                       [--hop-mode fused|serial|streams]
+                       [--hop-mode fused|serial|streams] [--hop-compare]
 """
 
 from __future__ import annotations
@@ -326,6 +326,60 @@ def measure_workloads(names=OTHER_WORKLOADS, reps: int = 3) -> list:
     return res
 
 
+def compare_hop_modes(name: str, passes: int = 3) -> dict:
+    """Forward call time of one workload under each hop schedule (fused,
+    serial, streams), interleaved over `passes` passes after an untimed one
+    (the order rotates, so that each schedule leads one pass),
+    without the library's per-launch timing events; the outputs of every
+    schedule must match the first bit for bit."""
+    import torch
+
+    import ring_attention_block_step_amd as ra
+    import workloads as wl
+
+    w = wl.WORKLOADS[name]
+    rank = w.ranks[-1]
+    k_glob, v_glob = wl.global_kv(w)
+    idx = ra.shard_index(w.N, w.P, w.layout, rank)
+    q = wl.query_rows(w, idx.numpy()).cuda()
+    k = ra.pack_shards(k_glob, w.P, w.layout).cuda()
+    v = ra.pack_shards(v_glob, w.P, w.layout).cuda()
+    del k_glob, v_glob
+    out = torch.empty_like(q)
+    lse = torch.empty((w.Hq, w.b), dtype=torch.float32, device="cuda")
+    n_timed = 20 if w.N <= 131072 else 2
+    res = {m: [] for m in ra.HOP_MODES}
+    ref = None
+    identical = True
+    try:
+        for mode in ra.HOP_MODES:   # an untimed pass: clocks and caches settle before any figure
+            ra.set_hop_mode(mode)
+            for _ in range(n_timed):
+                ra.forward(q, k, v, P=w.P, rank=rank, causal=w.causal, layout=w.layout, out=out, lse=lse)
+        torch.cuda.synchronize()
+        modes = list(ra.HOP_MODES)
+        for p in range(passes):
+            for mode in modes[p % 3:] + modes[:p % 3]:   # each schedule leads one pass
+                ra.set_hop_mode(mode)
+                for _ in range(2):
+                    ra.forward(q, k, v, P=w.P, rank=rank, causal=w.causal, layout=w.layout, out=out, lse=lse)
+                torch.cuda.synchronize()
+                if ref is None:
+                    ref = (out.clone(), lse.clone())
+                identical = identical and torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(n_timed):
+                    ra.forward(q, k, v, P=w.P, rank=rank, causal=w.causal, layout=w.layout, out=out, lse=lse)
+                e1.record()
+                torch.cuda.synchronize()
+                res[mode].append(e0.elapsed_time(e1) / n_timed)
+    finally:
+        ra.set_hop_mode("fused")
+    return {"workload": name, "ms_per_call": res, "calls_per_figure": n_timed, "bit_identical": identical}
+
+
 def measure_reference_gemm(n: int = 16384, reps: int = 10) -> dict:
     """Context for the MFMA roofline, not a step of the path: the vendor
     library's dense bf16 GEMM (torch.matmul, which dispatches to hipBLASLt) on
@@ -583,6 +637,8 @@ def main(argv=None) -> int:
                     help="only run the merge-kernel measurement and print its JSON object")
     ap.add_argument("--hop-mode", default="fused", choices=("fused", "serial", "streams"),
                     help="schedule of the ring's hop copies (ringattn_set_hop_mode)")
+    ap.add_argument("--hop-compare", action="store_true",
+                    help="only time the forward of --workload under each hop schedule and print a JSON object")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -613,6 +669,9 @@ def main(argv=None) -> int:
         return 0
     if args.copy_bytes:
         copy_calibration(args.copy_bytes)
+        return 0
+    if args.hop_compare:
+        print(json.dumps(compare_hop_modes(args.workload)), flush=True)
         return 0
     w = wl.WORKLOADS[args.workload]
     rank = w.ranks[-1]
