@@ -250,7 +250,13 @@ constexpr int kDkvPairs = 4;  // 4 pairs of waves x 32 keys = 128 keys per workg
 constexpr int kDkvWaves = 2 * kDkvPairs;
 constexpr int kXcds = 8;       // accelerator complex dies; workgroup L is dispatched to die L % 8
 constexpr int kDkvBufs = 6;    // LDS ring of query items: it-1 .. it+4 during iteration it
-constexpr int kXchBytes = 4096;  // packed P and dS of one item for one wave pair
+// P^T and dS^T of one item for one wave pair, each a row-major 32 (queries) x
+// 32 (keys) bf16 tile with a 72-byte row pitch: the score wave's 8-byte row
+// writes are free of bank conflicts, and the gradient wave reads columns
+// with ds_read_b64_tr_b16.
+constexpr int kXchPitch = 72;
+constexpr int kXchMat = 32 * kXchPitch;
+constexpr int kXchBytes = 2 * kXchMat;
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -393,10 +399,9 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   const int pb_lo = q_lo / 32;
   const int n_items = pb_lo < a.npb ? (a.npb - pb_lo) * a.G : 0;
 
-  // Mask (see BlockMask): query row i sees this lane's key iff i >= thr and
-  // i < b; an item whose rows all reach full_from sees every key of the pair.
-  const bool kin = key < a.b && key < a.kend;
-  const int thr = !kin ? INT_MAX : (a.shift >= 0 ? max(a.qbeg, key + a.shift) : a.qbeg);
+  // Mask (see BlockMask): an item whose rows all reach full_from sees every
+  // key of the pair; otherwise query row i sees the pair's keys below
+  // keys_seen(i) - k0.
   const int plast = k0 + 31;
   const int full_from =
       (plast < a.b && plast < a.kend) ? (a.shift >= 0 ? max(a.qbeg, plast + a.shift) : a.qbeg) : INT_MAX;
@@ -456,7 +461,7 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   };
   typedef const __attribute__((address_space(3))) float lds_f32;
   typedef const f32x4 __attribute__((address_space(3)))* lds_f4_ptr;
-  typedef bf16x8 __attribute__((address_space(3)))* lds_frag_wptr;
+  typedef u32x2 __attribute__((address_space(3)))* lds_u2_wptr;
   if (n_items == 0) return;   // dK, dV of these keys receive nothing from this visit
 
   if (scorer) {
@@ -474,8 +479,9 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
         vf[ks] = kb ? *reinterpret_cast<const bf16x8*>(a.v + base + ks * 16 + hi * 8) : zv;
       }
     }
-    // S = Q K^T and dP = dO V^T of an item: lane holds key l32, register r
-    // query 8(r/4) + 4hi + r%4.  Two register sets: iteration it turns the
+    // S^T = K Q^T and dP^T = V dO^T of an item (K, V fragments the A operand,
+    // the item's row fragments the B operand): lane holds query row l32,
+    // register r key 8(r/4) + 4hi + r%4 of the pair.  Two register sets: iteration it turns the
     // set of item it into P and dS while the MFMAs of item it+1 fill the
     // other.  The 2KS MFMAs alternate S and dP; each is followed by one
     // register's VALU work and the LDS read of the fragment kPF MFMAs later.
@@ -491,24 +497,27 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
       const lds_t* cur = buf(it);
       const lds_t* nxt = buf(it + 1);
       lds_f32* st = (lds_f32*)(cur + IT::STATS);
-      f32x4 l2v[4], ddv[4];
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        l2v[rg] = *(lds_f4_ptr)(st + 8 * rg + 4 * hi);
-        ddv[rg] = *(lds_f4_ptr)(st + 32 + 8 * rg + 4 * hi);
-      }
+      // Lane (l32, hi) holds query row q0 + l32 of the item: one LSE and one D.
+      const float l2 = st[l32];
+      const float dd = st[32 + l32];
       bf16x8 fr[kPF];
 #pragma unroll
       for (int j = 0; j < kPF; ++j) fr[j] = frag(nxt, j);
-      const int q0 = (pb_lo + it / a.G) * 32;
-      const int lo = thr - q0, hiq = a.b - q0;
-      bf16x8 pk[2], dk8[2];
+      // Keys of the pair this lane's query row sees: register r is key
+      // 8(r/4) + 4hi + r%4 of the pair, seen iff below kmax.
+      int kmax = 32;
+      if constexpr (MASKED) {
+        const int i = (pb_lo + it / a.G) * 32 + l32;
+        const int seen = (i >= a.b || i < a.qbeg) ? 0
+                         : min(min(a.kend, a.b), a.shift >= 0 ? i + 1 - a.shift : INT_MAX);
+        kmax = seen - k0;
+      }
+      u32x2 pk[4], gk[4];
       auto unit = [&](int r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(cs[r], a.sl2, -l2v[r >> 2][r & 3]));
-        float g = p * (cd[r] - ddv[r >> 2][r & 3]);
+        float p = __builtin_amdgcn_exp2f(fmaf(cs[r], a.sl2, -l2));
+        float g = p * (cd[r] - dd);
         if constexpr (MASKED) {
-          const int c = 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = c >= lo && c < hiq;
+          const bool ok = 8 * (r >> 2) + 4 * hi + (r & 3) < kmax;
           p = ok ? p : 0.f;
           g = ok ? g : 0.f;
         }
@@ -516,11 +525,8 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
         cd[r] = g;
         if (r & 1) {
           const f32x2 pp = {cs[r - 1], p}, gg = {cd[r - 1], g};
-          const bf16x2 a2 = __builtin_convertvector(pp, bf16x2), b2 = __builtin_convertvector(gg, bf16x2);
-          pk[r >> 3][(r & 7) - 1] = a2[0];
-          pk[r >> 3][r & 7] = a2[1];
-          dk8[r >> 3][(r & 7) - 1] = b2[0];
-          dk8[r >> 3][r & 7] = b2[1];
+          pk[r >> 2][(r & 3) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2));
+          gk[r >> 2][(r & 3) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(gg, bf16x2));
         }
       };
       auto group = [&](auto mc) {
@@ -528,12 +534,12 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
         constexpr int ks = m >> 1;
         bf16x8& f = fr[m % kPF];
         if constexpr (m & 1) {
-          if constexpr (ks == 0) nd = mfma(f, vf[0], f32x16{});
-          else nd = mfma(f, vf[ks], nd);
+          if constexpr (ks == 0) nd = mfma(vf[0], f, f32x16{});
+          else nd = mfma(vf[ks], f, nd);
           pin(nd);
         } else {
-          if constexpr (ks == 0) ns = mfma(f, kf[0], f32x16{});
-          else ns = mfma(f, kf[ks], ns);
+          if constexpr (ks == 0) ns = mfma(kf[0], f, f32x16{});
+          else ns = mfma(kf[ks], f, ns);
           pin(ns);
         }
 #pragma unroll
@@ -544,13 +550,13 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
       };
       [&]<int... ms>(std::integer_sequence<int, ms...>) { (group(std::integral_constant<int, ms>{}), ...); }
       (std::make_integer_sequence<int, NM>{});
-      // P, dS in the score register order, one 16-byte chunk per lane per
-      // group of 8 registers: chunk j of lane l at (64 j + l) * 16.
-      lds_t* xo = xch + (it & 1) * (kDkvPairs * kXchBytes) + pair * kXchBytes;
-      *reinterpret_cast<lds_frag_wptr>(xo + (0 * 64 + lane) * 16) = pk[0];
-      *reinterpret_cast<lds_frag_wptr>(xo + (1 * 64 + lane) * 16) = pk[1];
-      *reinterpret_cast<lds_frag_wptr>(xo + (2 * 64 + lane) * 16) = dk8[0];
-      *reinterpret_cast<lds_frag_wptr>(xo + (3 * 64 + lane) * 16) = dk8[1];
+      // P^T and dS^T rows: lane (l32, hi) writes keys 8g + 4hi .. +3 of row l32.
+      lds_t* xo = xch + (it & 1) * (kDkvPairs * kXchBytes) + pair * kXchBytes + l32 * kXchPitch + hi * 8;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        *reinterpret_cast<lds_u2_wptr>(xo + g4 * 16) = pk[g4];
+        *reinterpret_cast<lds_u2_wptr>(xo + kXchMat + g4 * 16) = gk[g4];
+      }
     };
     auto score = [&](int it, f32x16& cs, f32x16& cd, f32x16& ns, f32x16& nd) {
       iteration(it, [&](int it) {
@@ -567,8 +573,8 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) sA[r] = dA[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      sA = mfma(frag(buf(0), 2 * ks), kf[ks], sA);
-      dA = mfma(frag(buf(0), 2 * ks + 1), vf[ks], dA);
+      sA = mfma(kf[ks], frag(buf(0), 2 * ks), sA);
+      dA = mfma(vf[ks], frag(buf(0), 2 * ks + 1), dA);
     }
     for (int it = 0; it <= n_items; it += 2) {
       score(it, sA, dA, sB, dB);
@@ -592,11 +598,24 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
     // dV^T += dO^T P and dK^T += Q^T dS of item it-1.
     const lds_t* prev = buf(it - 1);
     const lds_t* xi = xch + ((it - 1) & 1) * (kDkvPairs * kXchBytes) + pair * kXchBytes;
+    // B operands P, dS (lane: key l32, the 8 queries of k-step kk in the
+    // order of the transposed item reads): columns of the P^T, dS^T tiles,
+    // read with the same transposed pattern as the item (rows are queries,
+    // the d of the item read is the key here).
     bf16x8 pb[2], db[2];
+    const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      pb[kk] = *reinterpret_cast<lds_frag_ptr>(xi + ((0 + kk) * 64 + lane) * 16);
-      db[kk] = *reinterpret_cast<lds_frag_ptr>(xi + ((2 + kk) * 64 + lane) * 16);
+      u32x2 hp[2], hd[2];
+#pragma unroll
+      for (int e4 = 0; e4 < 2; ++e4) {
+        const int row = 16 * kk + 8 * e4 + 4 * hi + (sl >> 2);
+        const int kc = 16 * (g & 1) + 4 * (sl & 3);
+        hp[e4] = lds_read_tr16(xi + row * kXchPitch + kc * 2);
+        hd[e4] = lds_read_tr16(xi + kXchMat + row * kXchPitch + kc * 2);
+      }
+      pb[kk] = __builtin_bit_cast(bf16x8, u32x4{hp[0][0], hp[0][1], hp[1][0], hp[1][1]});
+      db[kk] = __builtin_bit_cast(bf16x8, u32x4{hd[0][0], hd[0][1], hd[1][0], hd[1][1]});
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
