@@ -666,10 +666,10 @@ constexpr int kDqWaves = 8;    // 8 query items (32 rows each) per workgroup, on
 // V(t+2) and K^T(t+1) stream in.
 //
 // Tiles that every row of the workgroup sees in full run in a software
-// pipeline over half tiles h: block h issues the 8 MFMAs of dQ(h-1) with the
-// VALU work of half h in between (dS = P (dP - D), P = exp2(S log2e/sqrt(d) -
-// lse2), packed to bf16), then the 16 MFMAs of S, dP of half h+1 into the same
-// registers.  Each MFMA is followed by the LDS read of the fragment a later
+// pipeline over half tiles h: block h issues the 8 MFMAs of dQ(h-1) with
+// P = exp2(S log2e/sqrt(d) - lse2) of half h in between, then the 8 MFMAs of
+// S of half h+1 with dS = P (dP - D) of half h (packed to bf16) in between,
+// then the 8 MFMAs of dP of half h+1.  Each MFMA is followed by the LDS read of the fragment a later
 // MFMA takes.  The remaining tiles (causal diagonal, key end, shard end) are
 // folded one half at a time with the element mask.
 template <int D>
@@ -775,7 +775,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
   if (F > 0) {
     constexpr int NG = 2 * DT + 2 * KS;   // MFMAs per half-tile block
     constexpr int kPF = 4;                // fragment prefetch distance, in groups
-    constexpr int per = 16 / (2 * DT);    // VALU units per dQ group
+    constexpr int per = 16 / (2 * DT);    // probabilities per dQ group
+    constexpr int perS = 16 / KS;         // dS entries per S group
     f32x16 s, dp;
     bf16x8 dsA[2], dsB[2];
     bf16x8 fr[kPF];
@@ -829,10 +830,13 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
         else
           lds_read16_untracked<(2 * half + (m - NG) % 2) * 2 * TROW + ((m - NG) / 2) * 512>(f, tb_cur);
       };
-      auto unit = [&](int e) {
-        const float x = __builtin_amdgcn_exp2f(fmaf(s[e], a.sl2, -l2));
-        pv[e] = x;
-        dsv[e] = x * (dp[e] - drow);
+      // The VALU work of half h, spread over two thirds of the block: P from
+      // S between the dQ MFMAs (the first S MFMA of half h+1 overwrites S),
+      // dS = P (dP - D) and its bf16 pack between the S MFMAs (the first dP
+      // MFMA overwrites dP).
+      auto prob = [&](int e) { pv[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.sl2, -l2)); };
+      auto dsunit = [&](int e) {
+        dsv[e] = pv[e] * (dp[e] - drow);
         if (e & 1) {
           const f32x2 qq = {dsv[e - 1], dsv[e]};
           const bf16x2 pk = __builtin_convertvector(qq, bf16x2);
@@ -848,7 +852,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
           o[m / 2] = mfma(f, dsp[m % 2], o[m / 2]);
           pin(o[m / 2]);
 #pragma unroll
-          for (int u = 0; u < per; ++u) unit(m * per + u);
+          for (int u = 0; u < per; ++u) prob(m * per + u);
         } else if constexpr (m < 2 * DT + KS) {
           constexpr int ks = m - 2 * DT;
           if constexpr (ks == 0) {
@@ -857,6 +861,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
           }
           s = mfma(f, qf[ks], s);
           pin(s);
+#pragma unroll
+          for (int u = 0; u < perS; ++u) dsunit(ks * perS + u);
         } else {
           constexpr int ks = m - 2 * DT - KS;
           if constexpr (ks == 0) {
