@@ -258,7 +258,7 @@ int ringattn_redo_count(int64_t* redone, int64_t* redone_late_fold);
  *                        the dK/dV launch of visit i copies the block of
  *                        visit i+1 before its own work).  ringattn_forward_f32,
  *                        whose step kernel has no copy, uses
- *                        RINGATTN_HOP_STREAMS instead;
+ *                        RINGATTN_HOP_SERIAL instead;
  *   RINGATTN_HOP_SERIAL  a copy kernel on the caller's stream between steps;
  *   RINGATTN_HOP_STREAMS a copy kernel on the library's second stream beside
  *                        the next step, ordered by events.

@@ -208,7 +208,9 @@ int run_ring(int P, int rank, int b, int causal, int layout, size_t slot_bytes, 
   const int n = (int)visits.size();  // >= 1: the own block is never fully masked
 
   std::lock_guard<std::mutex> lk(ctx->mu);
-  const int mode = (g_hop_mode == RINGATTN_HOP_FUSED && !fusable) ? RINGATTN_HOP_STREAMS : g_hop_mode;
+  // A caller whose step kernel carries no copy runs the fused schedule's
+  // single-stream order with separate copies (no cross-stream events).
+  const int mode = (g_hop_mode == RINGATTN_HOP_FUSED && !fusable) ? RINGATTN_HOP_SERIAL : g_hop_mode;
   const bool streams = mode == RINGATTN_HOP_STREAMS;
   hipStream_t hs = streams ? ctx->hop : st;
 
