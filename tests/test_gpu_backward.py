@@ -144,17 +144,32 @@ def test_backward_medium_all_rows():
     _check("dv", gv.cpu().double().numpy(), wv, "medium rank 5")
 
 
-def test_backward_hop_modes_are_bit_identical():
-    N, P, Hq, Hkv, d = 1024, 4, 4, 2, 128
+@pytest.mark.parametrize("N,P,rank,Hq,Hkv,d,layout", [
+    (1024, 4, 3, 4, 2, 128, "contiguous"),
+    (1000, 4, 1, 4, 2, 64, "zigzag"),      # ragged b = 250: the last key tile is partial
+    (4096, 8, 5, 8, 1, 128, "striped"),    # GQA 8/1, two hop units per dK/dV workgroup
+])
+def test_backward_hop_modes_are_bit_identical(N, P, rank, Hq, Hkv, d, layout):
+    """The dQ kernel's double buffer must not race in any hop schedule: the
+    copies fused into the dK/dV launches, serialised on the caller stream, or
+    on the second stream give bit-identical gradients (O and LSE from the GPU
+    forward)."""
     q, k, v, do = _inputs(N, P, Hq, Hkv, d, seed=7)
+    b = N // P
+    tq = torch.as_tensor(oracle.shard_positions(layout, rank, P, b))
+    kp = ra.pack_shards(k, P, layout).cuda()
+    vp = ra.pack_shards(v, P, layout).cuda()
+    qr, dor = q[tq].cuda(), do[tq].cuda()
+    out, lse = ra.forward(qr, kp, vp, P=P, rank=rank, causal=True, layout=layout)
     res = []
-    for mode in ("fused", "serial", "streams"):
-        ra.set_hop_mode(mode)
-        try:
-            (gq, gk, gv), _ = _run_rank(q, k, v, do, N, P, 3, "contiguous", True, Hq, Hkv, d)
-        finally:
-            ra.set_hop_mode("fused")
-        res.append((gq.cpu(), gk.cpu(), gv.cpu()))
+    try:
+        for mode in ("fused", "serial", "streams", "fused"):
+            ra.set_hop_mode(mode)
+            g = ra.backward(qr, kp, vp, out, lse, dor, P=P, rank=rank, causal=True, layout=layout)
+            torch.cuda.synchronize()
+            res.append(tuple(t.cpu() for t in g))
+    finally:
+        ra.set_hop_mode("fused")
     for other in res[1:]:
         for a, b_ in zip(res[0], other):
             assert torch.equal(a, b_)
