@@ -147,7 +147,7 @@ def test_backward_medium_all_rows():
 @pytest.mark.parametrize("N,P,rank,Hq,Hkv,d,layout", [
     (1024, 4, 3, 4, 2, 128, "contiguous"),
     (1000, 4, 1, 4, 2, 64, "zigzag"),      # ragged b = 250: the last key tile is partial
-    (4096, 8, 5, 8, 1, 128, "striped"),    # GQA 8/1, two hop units per dK/dV workgroup
+    (16384, 8, 5, 8, 1, 128, "striped"),   # GQA 8/1, b = 2048: two hop units per dK/dV workgroup
 ])
 def test_backward_hop_modes_are_bit_identical(N, P, rank, Hq, Hkv, d, layout):
     """The dQ kernel's double buffer must not race in any hop schedule: the
