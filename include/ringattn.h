@@ -78,8 +78,9 @@ enum { RINGATTN_HOP_FUSED = 0, RINGATTN_HOP_SERIAL = 1, RINGATTN_HOP_STREAMS = 2
  *
  * The library allocates its workspace (two key/value slots and the fp32 running
  * state) stream-ordered on `stream` and frees it the same way.  The block for
- * step s+1 is copied into the free slot on a second, library-owned stream while
- * step s computes: the one-GPU stand-in for the ring hop.
+ * step s+1 is copied into the free slot while step s computes, by default by
+ * the step launch's own workgroups after their tiles (ringattn_set_hop_mode):
+ * the one-GPU stand-in for the ring hop.
  */
 int ringattn_forward(const void* q, const void* k, const void* v, void* out, float* lse,
                      int64_t N, int P, int rank, int Hq, int Hkv, int d_h,
@@ -118,7 +119,8 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
  *
  * The library allocates its workspace (the query rows' packed tiles and two
  * packed key/value slots) stream-ordered on `stream`; the slot of visit s+1 is
- * packed on the library's second stream while visit s computes.
+ * packed while visit s computes, by default by the dK/dV launch of visit s
+ * before its own work (ringattn_set_hop_mode).
  */
 int ringattn_backward(const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, float* dq, float* dk, float* dv,
