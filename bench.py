@@ -287,8 +287,8 @@ OTHER_WORKLOADS = ("32k-contiguous-causal", "32k-striped-causal", "32k-zigzag-ca
 def measure_workloads(names=OTHER_WORKLOADS, reps: int = 3) -> list:
     """The forward call on the other named bf16 workloads (the other shard
     layouts and sizes), timed like the main line: useful TFLOP/s per call.
-    Shares up to 128k tokens take 20 timed calls after 3 warm-up calls (a call
-    is a few ms), the larger ones `reps` after one."""
+    Shares up to 128k tokens take 20 timed calls after at least 3 warm-up calls
+    and 150 ms of them (a call is a few ms), the larger ones `reps` after one."""
     import torch
 
     import ring_attention_block_step_amd as ra
@@ -308,9 +308,15 @@ def measure_workloads(names=OTHER_WORKLOADS, reps: int = 3) -> list:
         lse = torch.empty((w.Hq, w.b), dtype=torch.float32, device="cuda")
         small = w.N <= 131072
         n_warm, n_timed = (3, 20) if small else (1, reps)
-        for _ in range(n_warm):
+        # Warm-up: at least n_warm calls and, for the small shares, 150 ms of
+        # them (the first ~0.1 s of work after an idle spell runs a few percent
+        # slow).
+        t_warm = time.perf_counter()
+        calls = 0
+        while calls < n_warm or (small and time.perf_counter() - t_warm < 0.15):
             ra.forward(q, k, v, P=w.P, rank=rank, causal=w.causal, layout=w.layout, out=out, lse=lse)
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            calls += 1
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
