@@ -119,8 +119,9 @@ int ringattn_forward_f32(const float* q, const float* k, const float* v, float* 
  *
  * The library allocates its workspace (the query rows' packed tiles and two
  * packed key/value slots) stream-ordered on `stream`; the slot of visit s+1 is
- * packed while visit s computes, by default by the dK/dV launch of visit s
- * before its own work (ringattn_set_hop_mode).
+ * packed while visit s computes, by default by the dK/dV workgroups of visit
+ * s's launch before their own work (ringattn_set_hop_mode).  Each visit is
+ * one launch whose workgroups compute either dK, dV or dQ.
  */
 int ringattn_backward(const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, float* dq, float* dk, float* dv,
@@ -224,8 +225,8 @@ int ringattn_timing_enable(int enable);
 int ringattn_timing_collect(double* step_ms, int64_t* step_launches,
                             double* merge_ms, int64_t* merge_launches);
 
-/* Same for the step kernels of ringattn_backward (the dK/dV and dQ kernels of
- * each visit together): summed duration (ms) and number of visits. */
+/* Same for the visit launches of ringattn_backward (dK/dV and dQ of a visit
+ * in one launch): summed duration (ms) and number of visits. */
 int ringattn_timing_collect_backward(double* step_ms, int64_t* step_launches);
 
 /* Same for ringattn_decode_partial calls: summed duration (ms) of the decode
@@ -257,8 +258,8 @@ int ringattn_redo_count(int64_t* redone, int64_t* redone_late_fold);
  *                        block of visit i+1, in its workgroups' tails, so the
  *                        copy overlaps the step inside one launch and no
  *                        cross-stream event is needed (ringattn_backward:
- *                        the dK/dV launch of visit i copies the block of
- *                        visit i+1 before its own work).  ringattn_forward_f32,
+ *                        the dK/dV workgroups of visit i's launch copy the
+ *                        block of visit i+1 before their own work).  ringattn_forward_f32,
  *                        whose step kernel has no copy, uses
  *                        RINGATTN_HOP_SERIAL instead;
  *   RINGATTN_HOP_SERIAL  a copy kernel on the caller's stream between steps;

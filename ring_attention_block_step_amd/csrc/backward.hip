@@ -17,18 +17,20 @@
 //                     both as row fragments (the A operand of S and dP) and,
 //                     with ds_read_b64_tr_b16, transposed (the A operand of
 //                     dK^T and dV^T);
-//   bwd_pack_kernel   per visit: the dQ kernel's key tiles of the visiting
-//                     block (K and V row-major, K^T);
-//   bwd_dkdv_kernel   per visit: pairs of waves own 32 keys of the block and
-//                     run over every query item that sees them: the score
-//                     wave (K and V fragments in registers) forms S = Q K^T,
+//   bwd_pack_kernel   the dQ workgroups' key tiles of the visiting block (K
+//                     and V row-major, K^T), for the first visit (the visit
+//                     launches copy the block of the visit after them);
+//   bwd_visit_kernel  per visit, two kinds of workgroup in one launch:
+//     dK/dV           pairs of waves own 32 keys of the block and run over
+//                     every query item that sees them: the score wave (K
+//                     and V fragments in registers) forms S = Q K^T,
 //                     dP = dO V^T, P and dS; the gradient wave folds
 //                     dV^T += dO^T P and dK^T += Q^T dS and at the end adds
 //                     into the caller's dK_r, dV_r;
-//   bwd_dq_kernel     per visit: a wave owns one query item (Q and dO
-//                     fragments in registers) and runs over the block's key
-//                     tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T,
-//                     with K, V and K^T tiles staged in LDS.
+//     dQ              a wave owns one query item (Q and dO fragments in
+//                     registers) and runs over the block's key tiles:
+//                     S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T, with K,
+//                     V and K^T tiles staged in LDS.
 #include <climits>
 #include <utility>
 
@@ -60,7 +62,7 @@ __host__ __device__ inline int perm16(int kappa) { return (kappa & 3) | ((kappa 
 //   [Q 32 x D][dO 32 x D][stats: lse2[32] (LSE * log2 e; +inf for a row that
 //   saw no key), then D[32]], padded to whole KB.
 // Q and dO are row-major (row = query, 2D bytes), each 16-byte chunk at an
-// XOR-swizzled position, so that both reads of the dK/dV kernel are free of
+// XOR-swizzled position, so that both reads of the dK/dV workgroups are free of
 // bank conflicts: the MFMA A-operand read (16 lanes = 16 consecutive rows, one
 // logical chunk) and the transposed read ds_read_b64_tr_b16 (4 consecutive
 // rows x 64 bytes per half wave) that gives the Q^T, dO^T operands.
@@ -77,7 +79,7 @@ struct Item {
   static __host__ __device__ __forceinline__ int off(int r, int c) { return r * (2 * D) + ((c ^ swz(r)) << 4); }
 };
 
-// Key tile block of the dQ kernel's slot (64 keys of one key/value head):
+// Key tile block of the dQ workgroups' slot (64 keys of one key/value head):
 //   [K row-major (key_tile_off)][V row-major (key_tile_off)][K^T (val_tile_off)]
 template <int D>
 struct KBlock {
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   }
 }
 
-// Slot of the dQ kernel: per key/value head, tiles of 64 keys holding K and V
+// Slot of the dQ workgroups: per key/value head, tiles of 64 keys holding K and V
 // row-major and K^T transposed (keys in storage order); rows b .. bpad-1 zero.
 // Tile t of head h by NTH threads (tid < NTH) with (T x (D + 8)) uint16 of LDS
 // at ks: every thread first loads all of its chunks, then stores them, then
@@ -349,12 +351,15 @@ struct ItemFrag {
 // the score waves read items it and it+1, the gradient waves item it-1, and
 // items it+2 .. it+4 are resident or in flight.
 template <int D>
-__global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
+constexpr int kDkvLds = kDkvBufs * Item<D>::BYTES + 2 * kDkvPairs * kXchBytes;
+
+// Workgroup bid of nwg dK/dV workgroups, with kDkvLds<D> bytes of LDS at smem_raw.
+template <int D>
+__device__ __forceinline__ void dkdv_workgroup(const BwdArgs& a, int bid, int nwg, unsigned char* smem_raw) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   using IT = Item<D>;
   using F = ItemFrag<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kDkvBufs * IT::BYTES + 2 * kDkvPairs * kXchBytes];
   lds_t* smem = (lds_t*)smem_raw;
   lds_t* xch = smem + kDkvBufs * IT::BYTES;
 
@@ -363,13 +368,13 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   const uint32_t lane16 = (uint32_t)(lane * 16);
 
   // The next visit's hop copy, before this launch's own work: (64-key tile,
-  // key/value head) units of the dQ kernel's slot spread over the
+  // key/value head) units of the dQ workgroups' slot spread over the
   // workgroups, in LDS that the item ring overwrites only after the barrier
   // that follows each unit.
-  static_assert(kKeyTile * (D + 8) * 2 <= (int)sizeof(smem_raw), "hop copy fits the item ring");
+  static_assert(kKeyTile * (D + 8) * 2 <= kDkvLds<D>, "hop copy fits the item ring");
   if (a.hop_k != nullptr) {
     const int units = (a.bpad / kKeyTile) * a.Hkv;
-    for (int u = (int)blockIdx.x; u < units; u += (int)gridDim.x) {
+    for (int u = bid; u < units; u += nwg) {
       bwd_pack_tile<D, 64 * kDkvWaves>(reinterpret_cast<const uint16_t*>(a.hop_k),
                                        reinterpret_cast<const uint16_t*>(a.hop_v),
                                        static_cast<unsigned char*>(a.hop_slot), a.b, a.bpad, a.Hkv, u / a.Hkv,
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   // stream the same head's query items share that XCD's L2.
   const int nkb = (a.b + 32 * kDkvPairs - 1) / (32 * kDkvPairs);
   const int per_xcd = (nkb * a.Hkv + kXcds - 1) / kXcds;
-  const int idx = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  const int idx = (bid % kXcds) * per_xcd + bid / kXcds;
   if (idx >= nkb * a.Hkv) return;
   const int kvh = idx / nkb;
   const int wk0 = (idx % nkb) * (32 * kDkvPairs);
@@ -673,14 +678,17 @@ constexpr int kDqWaves = 8;    // 8 query items (32 rows each) per workgroup, on
 // MFMA takes.  The remaining tiles (causal diagonal, key end, shard end) are
 // folded one half at a time with the element mask.
 template <int D>
-__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
+constexpr int kDqLds = 9 * KBlock<D>::TILE;
+
+// Workgroup bid of the dQ workgroups, with kDqLds<D> bytes of LDS at smem_raw.
+template <int D>
+__device__ __forceinline__ void dq_workgroup(const BwdArgs& a, int bid, unsigned char* smem_raw) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   using KB = KBlock<D>;
   constexpr int CT = KB::TILE / 1024;   // 1 KB chunks of one component tile
   static_assert(CT % kDqWaves == 0, "component tiles split evenly over the waves");
   constexpr int PWC = CT / kDqWaves;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[9 * KB::TILE];
   lds_t* smem = (lds_t*)smem_raw;
   auto kbuf = [&](int t) { return smem + (t % 3) * KB::TILE; };
   auto vbuf = [&](int t) { return smem + (3 + t % 3) * KB::TILE; };
@@ -690,8 +698,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const uint32_t lane16 = (uint32_t)(lane * 16);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int kvh = blockIdx.x % a.Hkv;
-  const int wgi = a.dq_wgs_per_head - 1 - (int)(blockIdx.x / a.Hkv);
+  const int kvh = bid % a.Hkv;
+  const int wgi = a.dq_wgs_per_head - 1 - bid / a.Hkv;
   const int item = wgi * kDqWaves + wave;
   const int items = a.G * a.npb;
   const bool active = item < items;
@@ -944,6 +952,24 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
+// One launch per visit: workgroups 0 .. n_kv-1 compute dK, dV (and carry
+// the next visit's hop copy), the rest compute dQ.  The two kinds read
+// nothing the other writes, so they run side by side; the dK/dV workgroups
+// come first, the longer ones, and the dQ workgroups fill the compute units
+// they leave, which on a causal diagonal (short dK/dV workgroups at the
+// block's end, short dQ workgroups at its start) balances the launch.
+template <int D>
+__global__ __launch_bounds__(64 * kDkvWaves) void bwd_visit_kernel(BwdArgs a, int n_kv) {
+  static_assert(kDkvWaves == kDqWaves, "both kinds of workgroup have the same shape");
+  constexpr int LDS = kDkvLds<D> > kDqLds<D> ? kDkvLds<D> : kDqLds<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS];
+  const int bid = (int)blockIdx.x;
+  if (bid < n_kv)
+    dkdv_workgroup<D>(a, bid, n_kv, smem_raw);
+  else
+    dq_workgroup<D>(a, bid - n_kv, smem_raw);
+}
+
 }  // namespace
 
 size_t bwd_item_bytes(int D) { return D == 128 ? Item<128>::BYTES : Item<64>::BYTES; }
@@ -974,15 +1000,14 @@ hipError_t launch_bwd_pack(const __bf16* k_shard, const __bf16* v_shard, void* s
 
 hipError_t launch_bwd_step(const BwdArgs& a, int D, hipStream_t st) {
   const int nkb = (a.b + 32 * kDkvPairs - 1) / (32 * kDkvPairs);
-  const dim3 gkv((unsigned)((nkb * a.Hkv + kXcds - 1) / kXcds * kXcds));
-  const dim3 gq((unsigned)(a.dq_wgs_per_head * a.Hkv));
-  if (D == 128) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gkv, dim3(64 * kDkvWaves), 0, st, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, gq, dim3(64 * kDqWaves), 0, st, a);
-  } else {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gkv, dim3(64 * kDkvWaves), 0, st, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, gq, dim3(64 * kDqWaves), 0, st, a);
-  }
+  // dK/dV workgroups rounded up to whole XCD rounds, so that dQ workgroup j
+  // (launch index n_kv + j) runs on XCD j % kXcds.
+  const int n_kv = (nkb * a.Hkv + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid((unsigned)(n_kv + a.dq_wgs_per_head * a.Hkv));
+  if (D == 128)
+    hipLaunchKernelGGL(bwd_visit_kernel<128>, grid, dim3(64 * kDkvWaves), 0, st, a, n_kv);
+  else
+    hipLaunchKernelGGL(bwd_visit_kernel<64>, grid, dim3(64 * kDkvWaves), 0, st, a, n_kv);
   return hipGetLastError();
 }
 

@@ -92,7 +92,7 @@ struct BwdArgs {
   const float* lse;     // [Hq, b] LSE saved by the forward (natural log)
   const __bf16* k;      // [b, Hkv, D] visiting shard's keys (raw layout)
   const __bf16* v;      // [b, Hkv, D] visiting shard's values
-  const void* kslot;    // visiting shard packed for the dQ kernel: [Hkv][bpad/64] key blocks
+  const void* kslot;    // visiting shard packed for the dQ workgroups: [Hkv][bpad/64] key blocks
   void* items;          // [Hq][npb] query item blocks (written by the preparation kernel)
   float* dq;            // [b, Hq, D] dL/dQ of the rank's rows
   float* dk;            // [b, Hkv, D] visiting shard's dL/dK (accumulated)
@@ -103,8 +103,9 @@ struct BwdArgs {
   int dq_accumulate;              // add into dq (later visits) instead of writing it
   float sl2;                      // log2(e) / sqrt(D)
   float scale;                    // 1 / sqrt(D)
-  // Hop copy the dK/dV launch carries: the next visit's shard into the free
-  // dQ-kernel slot (the layout bwd_pack_kernel writes).  hop_k == null: none.
+  // Hop copy the dK/dV workgroups of a visit launch carry: the next visit's
+  // shard into the free dQ slot (the layout bwd_pack_kernel writes).
+  // hop_k == null: none.
   const __bf16* hop_k;
   const __bf16* hop_v;
   void* hop_slot;

@@ -150,8 +150,9 @@ def test_backward_medium_all_rows():
     (16384, 8, 5, 8, 1, 128, "striped"),   # GQA 8/1, b = 2048: two hop units per dK/dV workgroup
 ])
 def test_backward_hop_modes_are_bit_identical(N, P, rank, Hq, Hkv, d, layout):
-    """The dQ kernel's double buffer must not race in any hop schedule: the
-    copies fused into the dK/dV launches, serialised on the caller stream, or
+    """The dQ workgroups' double buffer must not race in any hop schedule: the
+    copies made by the dK/dV workgroups of each visit launch (beside the dQ
+    workgroups reading the other slot), serialised on the caller stream, or
     on the second stream give bit-identical gradients (O and LSE from the GPU
     forward)."""
     q, k, v, do = _inputs(N, P, Hq, Hkv, d, seed=7)
