@@ -465,7 +465,6 @@ __device__ __forceinline__ void dkdv_workgroup(const BwdArgs& a, int bid, int nw
     wait_items_and_sync();
   };
   typedef const __attribute__((address_space(3))) float lds_f32;
-  typedef const f32x4 __attribute__((address_space(3)))* lds_f4_ptr;
   typedef u32x2 __attribute__((address_space(3)))* lds_u2_wptr;
   if (n_items == 0) return;   // dK, dV of these keys receive nothing from this visit
 
