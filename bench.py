@@ -30,7 +30,8 @@ against 8 TB/s, the merge with the HBM bytes its counters measured
 useful TFLOP/s.  ``same_launches_on_constant_inputs`` times the headline
 launches again on operands that do not toggle (Q = K = 0, V = 1), with the
 engine clock then held: the rate the kernel's schedule sustains when the power
-limit does not lower the clock (context, not the metric).
+limit does not lower the clock (context, not the metric); the ``backward``
+object carries the same diagnostic for the backward calls.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--cpu-seconds S] [--no-cpu-baseline] [--no-merge]
@@ -494,10 +495,12 @@ def backward_useful_flops(pairs: int, d: int, heads: int) -> float:
     return 10.0 * d * pairs * heads
 
 
-def measure_backward(name: str = "32k-contiguous-causal", reps: int = 3) -> dict:
+def measure_backward(name: str = "32k-contiguous-causal", reps: int = 3, constant_inputs: bool = False) -> dict:
     """Time ringattn_backward for the workload's rank (inputs: the GPU
     forward's O and LSE, a seeded upstream gradient) and report useful
-    TFLOP/s per call and per step-kernel time against the bf16 peak."""
+    TFLOP/s per call and per step-kernel time against the bf16 peak, with the
+    engine clock.  constant_inputs: also time the same calls on operands that
+    do not toggle (Q = K = 0, V = 1, dO = 1), a clock/power diagnostic."""
     import torch
 
     import ring_attention_block_step_amd as ra
@@ -532,23 +535,50 @@ def measure_backward(name: str = "32k-contiguous-causal", reps: int = 3) -> dict
     ra.timing_enable(True)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        ra.backward(q, kp, vp, out, lse, do, P=w.P, rank=rank, causal=w.causal, layout=w.layout, dq=dq, dk=dk,
-                    dv=dv)
-    t1.record()
-    torch.cuda.synchronize()
+    clock = ClockSampler()
+    with clock:
+        t0.record()
+        for _ in range(reps):
+            ra.backward(q, kp, vp, out, lse, do, P=w.P, rank=rank, causal=w.causal, layout=w.layout, dq=dq, dk=dk,
+                        dv=dv)
+        t1.record()
+        torch.cuda.synchronize()
     ra.timing_enable(False)
     t = ra.timing_collect_backward()
     ms = t0.elapsed_time(t1) / reps
     flops = backward_useful_flops(useful_pairs(w.layout, rank, w.P, w.b, w.causal), w.d, w.Hq)
     kern_ms = t["step_ms"] / reps
+    sclk = clock.summary()
+    const = None
+    if constant_inputs:
+        zq, zk, ov, od = torch.zeros_like(q), torch.zeros_like(kp), torch.ones_like(vp), torch.ones_like(do)
+        cout, clse = ra.forward(zq, zk, ov, P=w.P, rank=rank, causal=w.causal, layout=w.layout)
+        for _ in range(2):
+            ra.backward(zq, zk, ov, cout, clse, od, P=w.P, rank=rank, causal=w.causal, layout=w.layout, dq=dq,
+                        dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        cclock = ClockSampler()
+        with cclock:
+            t0.record()
+            for _ in range(reps):
+                ra.backward(zq, zk, ov, cout, clse, od, P=w.P, rank=rank, causal=w.causal, layout=w.layout, dq=dq,
+                            dk=dk, dv=dv)
+            t1.record()
+            torch.cuda.synchronize()
+        cms = t0.elapsed_time(t1) / reps
+        cs = cclock.summary()
+        const = {"inputs": "Q = K = 0, V = 1, dO = 1", "calls": reps, "ms_per_call": cms,
+                 "value": flops / (cms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                 "frac_of_bf16_peak": flops / (cms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                 "sclk_mean_mhz": cs["mean_mhz"] if cs else None,
+                 "note": "same calls on non-toggling operands: the clock the power limit allows rises; not the metric"}
     return {"workload": name, "rank": rank, "useful_flops": flops, "ms_per_call": ms,
             "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
             "kernels": "bwd_visit_kernel<128> (dK/dV and dQ workgroups)", "kernel_ms_per_call": kern_ms,
             "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
             "frac": flops / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "visits_per_call": t["step_launches"] / reps,
-            "calls": reps,
+            "calls": reps, "sclk_mean_mhz": sclk["mean_mhz"] if sclk else None,
+            "same_calls_on_constant_inputs": const,
             "note": "useful = 5 contractions per allowed pair; the kernels run 7 (the dQ workgroups recompute S, dP)"}
 
 
@@ -808,7 +838,8 @@ def main(argv=None) -> int:
     attn_ref = None if args.no_gemm_ref else measure_reference_attention()
     others = None if args.no_workloads else measure_workloads()
     decode = None if args.no_decode else measure_decode(args.decode_workload)
-    backward = None if args.no_backward else measure_backward(args.backward_workload, reps=10)
+    backward = None if args.no_backward else measure_backward(args.backward_workload, reps=10,
+                                                              constant_inputs=not args.no_constant_inputs)
     backward_other = None
     if not args.no_backward and not args.no_workloads:
         backward_other = [measure_backward(n, reps=2) for n in BACKWARD_OTHER_WORKLOADS if n != args.backward_workload]
