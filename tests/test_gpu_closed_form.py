@@ -65,7 +65,7 @@ def test_forward_constant_operands_every_row(name):
     assert err.max() <= 6e-6, err.max()
 
 
-BACKWARD = ["32k-contiguous-causal", "128k-contiguous-causal"]
+BACKWARD = ["32k-contiguous-causal", "32k-striped-causal", "32k-zigzag-causal", "128k-contiguous-causal"]
 
 
 @pytest.mark.parametrize("name", BACKWARD)
