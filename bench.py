@@ -414,9 +414,29 @@ def measure_reference_gemm(n: int = 16384, reps: int = 10) -> dict:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    # The same GEMM on constant operands (all ones): no operand toggles, so
+    # the clock the power limit allows rises (compare the attention launches'
+    # same_launches_on_constant_inputs).
+    a.fill_(1.0)
+    b.fill_(1.0)
+    for _ in range(2):
+        c = a @ b
+    torch.cuda.synchronize()
+    clock = ClockSampler()
+    with clock:
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+    cms = e0.elapsed_time(e1) / reps
+    ctf = 2.0 * n ** 3 / (cms * 1e-3) / 1e12
+    cs = clock.summary()
     del a, b, c
     return {"op": "bf16 GEMM (torch.matmul -> hipBLASLt), fp32 accumulate", "shape": [n, n, n], "ms": ms,
-            "value": tflops, "unit": "TFLOP/s", "frac_of_peak": tflops / PEAK_BF16_TFLOPS}
+            "value": tflops, "unit": "TFLOP/s", "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
+            "constant_operands": {"inputs": "all ones", "ms": cms, "value": ctf, "frac_of_peak": ctf / PEAK_BF16_TFLOPS,
+                                  "sclk_mean_mhz": cs["mean_mhz"] if cs else None}}
 
 
 def measure_reference_attention(heads: int = 32, seq: int = 16384, d: int = 128, reps: int = 5) -> dict | None:
